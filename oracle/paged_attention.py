@@ -1,0 +1,254 @@
+"""Paged grouped-query decode attention, written out by its definition.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Slow on purpose:
+per-sequence numpy gathers and float64 arithmetic, no blocking or fusion
+beyond what the definition states.
+
+The computation (pages cited by title and section):
+
+* The KV cache is a pool of fixed-size blocks; a per-sequence block table
+  maps logical block j of a sequence to a physical block in the pool, and a
+  step first writes the new token's K/V at its write position, then reads
+  the sequence's blocks ("rvllm - A Small LLM Inference Engine in Rust",
+  section "How it's put together"; "rvLLM: High-performance LLM inference in
+  Rust", section "CUDA Kernels", rows "Reshape and Cache" and
+  "PagedAttention V2").
+* Each KV head is shared by a group of query heads ("rvllm - A Small LLM
+  Inference Engine in Rust", section "How it's put together"; "LLM Serving
+  Kernels", section "Projects", row 04 "GQA/MQA").
+* Online softmax ("PagedAttention V2 ... online softmax"; project 04) reaches,
+  up to rounding order, the plain softmax(q K^T * scale) V of one query
+  against the gathered context; that plain form is what this module computes.
+* Split-context ("flash-decoding") partials: each partition of the context
+  yields its own normalised output and log-sum-exp, and a log-sum-exp
+  weighted merge of the partials equals the full softmax.  The pages do not
+  describe this step; it is the plain algebra of the softmax over a disjoint
+  cover of the context.
+
+Byte layout of the pool (the library's documented format; this module reads
+and writes it with its own index arithmetic):
+
+* a K or V cache is ``[num_blocks, num_kv_heads, tile]`` where one tile holds
+  the 16 token slots x ``head_dim`` elements of one (block, kv head);
+* element size e bytes (4 f32, 2 f16/bf16, 1 e4m3);
+* K tile, with x = 16 / e elements per 16-byte chunk: element (t, d) sits at
+  ``((d // x) * 16 + t) * x + d % x``;
+* V tile, with n = 4 / e: element (t, d) sits at
+  ``(((((d // (16 n)) * 4 + t // 4) * 16 + d % 16) * n + (d // 16) % n) * 4 + t % 4``;
+* a slot number is ``block * 16 + offset``.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import e4m3
+
+BLOCK_SIZE = 16
+
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
+RAW_DTYPE = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8}
+# NaN bit patterns used to fill every slot no sequence owns.
+POISON = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "e4m3": 0x7F}
+
+
+# ---------------------------------------------------------------- values ---
+
+def to_f64(raw: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 values of raw storage bits."""
+    raw = np.asarray(raw)
+    if dtype == "f32":
+        return raw.astype(np.uint32).view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return raw.astype(np.uint16).view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        return (raw.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if dtype == "e4m3":
+        return e4m3.decode(raw.astype(np.uint8))
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------- layout ---
+
+def k_tile_index(head_dim: int, dtype: str) -> np.ndarray:
+    """int64 [16, D]: element offset of (token slot t, dim d) in a K tile."""
+    x = 16 // ELEM_BYTES[dtype]
+    t = np.arange(BLOCK_SIZE)[:, None]
+    d = np.arange(head_dim)[None, :]
+    return ((d // x) * BLOCK_SIZE + t) * x + d % x
+
+
+def v_tile_index(head_dim: int, dtype: str) -> np.ndarray:
+    """int64 [16, D]: element offset of (token slot t, dim d) in a V tile."""
+    n = 4 // ELEM_BYTES[dtype]
+    t = np.arange(BLOCK_SIZE)[:, None]
+    d = np.arange(head_dim)[None, :]
+    return (((((d // (16 * n)) * 4 + t // 4) * 16 + d % 16) * n + (d // 16) % n) * 4 + t % 4)
+
+
+def new_pool(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str):
+    """A K and a V cache filled with the dtype's NaN pattern."""
+    shape = (num_blocks, num_kv_heads, BLOCK_SIZE * head_dim)
+    k = np.full(shape, POISON[dtype], dtype=RAW_DTYPE[dtype])
+    v = np.full(shape, POISON[dtype], dtype=RAW_DTYPE[dtype])
+    return k, v
+
+
+# ----------------------------------------------------------------- write ---
+
+def kv_cache_write(k_cache, v_cache, k_raw, v_raw, slot_mapping, dtype: str) -> None:
+    """Copy token t's K/V [Hkv, D] bits into its slot; negative slots skip.
+
+    "rvLLM: High-performance LLM inference in Rust", section "CUDA Kernels",
+    row "Reshape and Cache"; "rvllm - A Small LLM Inference Engine in Rust",
+    section "How it's put together" (write_positions).
+    """
+    head_dim = k_raw.shape[-1]
+    kidx = k_tile_index(head_dim, dtype)
+    vidx = v_tile_index(head_dim, dtype)
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0:
+            continue
+        blk, off = int(slot) // BLOCK_SIZE, int(slot) % BLOCK_SIZE
+        k_cache[blk][:, kidx[off]] = k_raw[t]
+        v_cache[blk][:, vidx[off]] = v_raw[t]
+
+
+def kv_cache_write_e4m3_blocks(k_cache, v_cache, kv_scales, k_blocks, v_blocks,
+                               block_ids, valid_tokens) -> None:
+    """Quantise whole blocks of fp32 K/V to E4M3 and store codes and scales.
+
+    ``k_blocks``/``v_blocks``: float32 [n, 16, Hkv, D] (slot order);
+    ``block_ids``: [n] physical block ids; ``valid_tokens``: [n] leading slots
+    that hold data.  ``kv_scales`` is float32 [2, num_blocks, Hkv] (0 = K,
+    1 = V).  Slots at or past ``valid_tokens`` receive code 0.
+    """
+    head_dim = k_blocks.shape[-1]
+    kidx = k_tile_index(head_dim, "e4m3")
+    vidx = v_tile_index(head_dim, "e4m3")
+    kc, ks = e4m3.quantize_blocks(k_blocks, valid_tokens)
+    vc, vs = e4m3.quantize_blocks(v_blocks, valid_tokens)
+    for i, blk in enumerate(np.asarray(block_ids, dtype=np.int64)):
+        for t in range(BLOCK_SIZE):
+            k_cache[blk][:, kidx[t]] = kc[i, t]
+            v_cache[blk][:, vidx[t]] = vc[i, t]
+        kv_scales[0, blk] = ks[i]
+        kv_scales[1, blk] = vs[i]
+
+
+# ---------------------------------------------------------------- gather ---
+
+def gather(k_cache, v_cache, kv_dtype: str, table_row, context_len: int,
+           kv_head: int, head_dim: int, kv_scales=None):
+    """Dense float64 K and V [L, D] of one sequence and one KV head.
+
+    Token t lives in physical block table_row[t // 16] at offset t % 16
+    ("rvllm - A Small LLM Inference Engine in Rust", section "How it's put
+    together": read_blocks + read_num_tokens).  For E4M3 each value is the
+    decoded code times its block's K or V scale ("LLM Serving Kernels",
+    section "Projects", row 05).
+    """
+    kidx = k_tile_index(head_dim, kv_dtype)
+    vidx = v_tile_index(head_dim, kv_dtype)
+    L = int(context_len)
+    t = np.arange(L)
+    blk = np.asarray(table_row, dtype=np.int64)[t // BLOCK_SIZE]   # physical block of token t
+    off = t % BLOCK_SIZE                                             # its slot in that block
+    rows = t[:, None]
+    K = to_f64(k_cache[blk, kv_head][rows, kidx[off]], kv_dtype)
+    V = to_f64(v_cache[blk, kv_head][rows, vidx[off]], kv_dtype)
+    if kv_dtype == "e4m3":
+        K = K * kv_scales[0, blk, kv_head].astype(np.float64)[:, None]
+        V = V * kv_scales[1, blk, kv_head].astype(np.float64)[:, None]
+    return K, V
+
+
+# ------------------------------------------------------------- attention ---
+
+def softmax_weights(q_vec, K, scale: float) -> np.ndarray:
+    """p_t = exp(s_t - max s) / sum_u exp(s_u - max s), s_t = scale * q.K[t]."""
+    s = scale * (K @ q_vec)
+    e = np.exp(s - np.max(s))
+    return e / np.sum(e)
+
+
+def decode_attention(q_raw, q_dtype: str, k_cache, v_cache, kv_dtype: str,
+                     block_tables, context_lens, scale: float, kv_scales=None):
+    """float64 [B, Hq, D]: softmax(q K^T * scale) V per sequence and query head.
+
+    Query head i reads KV head i // G with G = Hq / Hkv (contiguous groups).
+    A sequence with context length 0 yields zeros.
+    """
+    q = to_f64(q_raw, q_dtype)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(context_lens[b])
+        if L == 0:
+            continue
+        for h in range(Hkv):
+            K, V = gather(k_cache, v_cache, kv_dtype, block_tables[b], L, h, D, kv_scales)
+            for g in range(G):
+                i = h * G + g
+                out[b, i] = softmax_weights(q[b, i], K, scale) @ V
+    return out
+
+
+def num_partitions(context_len: int, partition_size: int) -> int:
+    return (int(context_len) + partition_size - 1) // partition_size
+
+
+def decode_partials(q_raw, q_dtype: str, k_cache, v_cache, kv_dtype: str,
+                    block_tables, context_lens, scale: float, partition_size: int,
+                    num_slots: int, kv_scales=None):
+    """Per-partition outputs and log-sum-exps.
+
+    Partition j of sequence b covers tokens [j P, min((j+1) P, L_b)).  For it:
+    o_j = softmax over those tokens of the scaled logits, times their V;
+    lse_j = log sum_t exp(s_t) over those tokens (natural log).  Partitions at
+    or past ceil(L_b / P) are empty: o = 0 and lse = -inf.
+
+    Returns ``(o float64 [B, Hq, num_slots, D], lse float64 [B, Hq, num_slots])``.
+    """
+    q = to_f64(q_raw, q_dtype)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, num_slots, D), dtype=np.float64)
+    lse = np.full((B, Hq, num_slots), -np.inf, dtype=np.float64)
+    for b in range(B):
+        L = int(context_lens[b])
+        for h in range(Hkv):
+            K, V = gather(k_cache, v_cache, kv_dtype, block_tables[b], L, h, D, kv_scales)
+            for g in range(G):
+                i = h * G + g
+                s_all = scale * (K @ q[b, i])
+                for j in range(num_partitions(L, partition_size)):
+                    lo, hi = j * partition_size, min((j + 1) * partition_size, L)
+                    s = s_all[lo:hi]
+                    m = np.max(s)
+                    e = np.exp(s - m)
+                    o[b, i, j] = (e / np.sum(e)) @ V[lo:hi]
+                    lse[b, i, j] = m + math.log(np.sum(e))
+    return o, lse
+
+
+def merge_partials(o, lse, context_lens, partition_size: int) -> np.ndarray:
+    """LSE-weighted merge: out = sum_j w_j o_j / sum_j w_j, w_j = exp(lse_j - max lse).
+
+    Only partitions j < ceil(L_b / P) take part; L_b = 0 yields zeros.
+    """
+    B, Hq, _, D = o.shape
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        n = num_partitions(context_lens[b], partition_size)
+        if n == 0:
+            continue
+        for i in range(Hq):
+            l = lse[b, i, :n]
+            w = np.exp(l - np.max(l))
+            out[b, i] = (w @ o[b, i, :n]) / np.sum(w)
+    return out
