@@ -1,0 +1,210 @@
+/*
+ * pagedkv.h - C ABI of libpagedkv.so: paged grouped-query decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step of an LLM serving engine, per attention layer: every
+ * running sequence contributes one query token; its new K/V is first written
+ * into its slot of a pool of fixed-size KV blocks, then its query heads
+ * attend, with grouped-query heads, over the K/V reached through the
+ * sequence's block table, using online softmax.  Sources (by title and
+ * section):
+ *   - "rvLLM: High-performance LLM inference in Rust", section "CUDA
+ *     Kernels": PagedAttention V2 (block-table indirection, online softmax),
+ *     Reshape and Cache (write the new K/V into the paged cache), FP8 KV Cache
+ *     (E4M3 quantisation/dequantisation with per-head scaling).
+ *   - "rvllm - A Small LLM Inference Engine in Rust", section "How it's put
+ *     together": the KV cache is a pool of fixed-size blocks, each step takes
+ *     explicit write positions and read blocks; each KV head is shared by a
+ *     group of query heads.
+ *   - "LLM Serving Kernels", section "Projects": project 04 (page tables,
+ *     GQA/MQA, online softmax), project 05 (E4M3 storage, page scales, fused
+ *     dequantisation).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *   - All tensor pointers are device pointers owned by the caller, contiguous
+ *     row-major.  The library never allocates, frees or synchronises, keeps no
+ *     pointer after it returns, and enqueues all work on `stream` (a
+ *     hipStream_t; NULL is the default stream).
+ *   - Return value: PKV_OK (0) on success, else an error code; the message of
+ *     the last error on the calling thread is returned by pkv_last_error().
+ *     Arguments are checked on the host before anything is enqueued; on an
+ *     error nothing is enqueued.  PKV_ERR_HIP reports a failed launch.
+ *   - Values that live in device memory (block ids, context lengths, slots)
+ *     are not read by the host.  Their ranges are preconditions:
+ *     0 <= block id < num_blocks, 0 <= context_lens[b] <= max_blocks_per_seq*16,
+ *     slots unique and < num_blocks*16.  The kernels clamp a context length
+ *     to max_blocks_per_seq*16 and skip out-of-range slots; a block id out
+ *     of range is undefined behaviour.
+ *
+ * Shapes and names
+ * ----------------
+ *   B = num_seqs, Hq = num_q_heads, Hkv = num_kv_heads, G = Hq / Hkv (query
+ *   head i reads KV head i / G: contiguous groups), D = head_dim,
+ *   NB = num_blocks, MBPS = max_blocks_per_seq, block_size = 16 tokens.
+ *
+ * KV cache byte layout (k_cache and v_cache are [NB][Hkv][tile])
+ * ---------------------------------------------------------------
+ *   One tile holds the 16 token slots x D elements of one (block, kv head),
+ *   16*D*e bytes with e = element size (4 f32, 2 f16/bf16, 1 e4m3).  Slot s
+ *   is token offset s % 16 of block s / 16.  Inside a tile:
+ *     K: element (t, d) at ((d / x) * 16 + t) * x + d % x,   x = 16 / e
+ *        (16-byte chunks of one token's dims; the 16 tokens of one chunk
+ *        index are adjacent);
+ *     V: element (t, d) at ((((d / (16n)) * 4 + t / 4) * 16 + d % 16) * n
+ *                             + (d / 16) % n) * 4 + t % 4,   n = 4 / e
+ *        (groups of 4 consecutive tokens of one dim are adjacent).
+ *   Both place each 64-lane wave's 16-byte loads on one contiguous 1 KiB and
+ *   hand the matrix cores their operands without a transpose.
+ *
+ * Supported combinations (q / KV / out): f32/f32/f32; f16/f16/{f32,f16};
+ * bf16/bf16/{f32,bf16}; f16/e4m3/{f32,f16}.  D in {64, 128}, G in 1..16,
+ * block_size 16.
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad partition size, non-finite scale */
+  PKV_ERR_UNSUPPORTED = 2, /* dtype combination, head_dim or group size not built */
+  PKV_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+};
+
+enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_E4M3 = 3 };
+
+/* Sizes and element types of one decode-attention problem.  */
+typedef struct pkv_desc {
+  int32_t num_seqs;           /* B >= 0 (0: nothing to do)                    */
+  int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads               */
+  int32_t num_kv_heads;       /* Hkv >= 1                                     */
+  int32_t head_dim;           /* D: 64 or 128                                 */
+  int32_t block_size;         /* tokens per block: must be 16                 */
+  int32_t num_blocks;         /* NB: blocks in the pool                       */
+  int32_t max_blocks_per_seq; /* MBPS: row length of block_tables (>= 1)      */
+  int32_t q_dtype;            /* pkv_dtype of q (and of k/v for the write)    */
+  int32_t kv_dtype;           /* pkv_dtype of the caches                      */
+  int32_t out_dtype;          /* pkv_dtype of out                             */
+} pkv_desc;
+
+/*
+ * kv_cache_write - write each new token's K and V into its cache slot
+ * ("rvLLM: High-performance LLM inference in Rust", section "CUDA Kernels",
+ * row "Reshape and Cache"; "rvllm - A Small LLM Inference Engine in Rust",
+ * section "How it's put together", write_positions).
+ *
+ *   k, v          [num_tokens][Hkv][D] in kv_dtype (f32, f16 or bf16)
+ *   slot_mapping  int64 [num_tokens]; token t goes to slot slot_mapping[t];
+ *                 a negative slot skips the token
+ *   k_cache, v_cache  the pool, layout above; only the named slots change
+ * Bitwise copy.  Two tokens naming the same slot: which one lands is
+ * unspecified.  An e4m3 cache returns PKV_ERR_UNSUPPORTED (use
+ * kv_cache_quantize_e4m3 for whole blocks).
+ */
+int kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
+                   int64_t num_tokens, void* k_cache, void* v_cache,
+                   const pkv_desc* desc, void* stream);
+
+/*
+ * kv_cache_quantize_e4m3 - quantise whole blocks of fp32 K and V into an
+ * e4m3 pool, one fp32 scale per (block, kv head) for K and one for V ("LLM
+ * Serving Kernels", section "Projects", row 05: E4M3 storage, page scales;
+ * "rvLLM: High-performance LLM inference in Rust", section "CUDA Kernels",
+ * row "FP8 KV Cache": per-head scaling).
+ *
+ *   k_src, v_src    fp32 [num_src_blocks][16][Hkv][D]: the 16 token slots of
+ *                   each source block in slot order
+ *   block_ids       int32 [num_src_blocks]: destination block of each
+ *   valid_tokens    int32 [num_src_blocks]: leading slots holding data; the
+ *                   rest are ignored for the scale and receive code 0
+ *   k_cache, v_cache  e4m3 pool (desc->kv_dtype must be PKV_E4M3)
+ *   kv_scales       fp32 [2][NB][Hkv]; entry (0|1, block, head) is written
+ * scale = fp32(amax / 448) over the valid slots of (block, kv head), 1 when
+ * amax is 0; code = nearest-even OCP E4M3 (max 448) of clamp(fp32(x /
+ * scale), -448, 448).  Distinct block_ids are required.
+ */
+int kv_cache_quantize_e4m3(const float* k_src, const float* v_src, const int32_t* block_ids,
+                           const int32_t* valid_tokens, int32_t num_src_blocks, void* k_cache,
+                           void* v_cache, float* kv_scales, const pkv_desc* desc, void* stream);
+
+/*
+ * paged_decode_attention - one decode step of attention for every sequence
+ * in one pass: out[b][i] = softmax(q[b][i] . K_b^T * scale) V_b, where K_b,
+ * V_b are the first context_lens[b] tokens of sequence b gathered through
+ * block_tables[b] for KV head i / G ("rvLLM: High-performance LLM inference
+ * in Rust", section "CUDA Kernels", row "PagedAttention V2"; "LLM Serving
+ * Kernels", section "Projects", row 04).
+ *
+ *   q             [B][Hq][D] in q_dtype
+ *   k_cache, v_cache  [NB][Hkv][tile] in kv_dtype
+ *   block_tables  int32 [B][MBPS]; entries past ceil(context_lens[b]/16)
+ *                 are never read
+ *   context_lens  int32 [B]; includes the token written this step; a
+ *                 sequence with 0 gets a zero output
+ *   scale         softmax scale (finite), usually 1/sqrt(D)
+ *   kv_scales     e4m3 caches only, else NULL: fp32 [2][NB][Hkv], the K (0)
+ *                 and V (1) scale of each (block, kv head); the value of a
+ *                 code c is decode(c) * scale ("LLM Serving Kernels",
+ *                 "Projects", row 05: page scales, fused dequantisation)
+ *   out           [B][Hq][D] in out_dtype
+ * One workgroup per (sequence, kv head): suited to short contexts or many
+ * sequences; for long contexts use the partial/reduce pair.
+ */
+int paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           float scale, const float* kv_scales, void* out,
+                           const pkv_desc* desc, void* stream);
+
+/*
+ * paged_decode_attention_partial - split-context ("flash-decoding") first
+ * half: the context of each sequence is cut into partitions of
+ * partition_size tokens, and each (sequence, query head, partition) yields
+ * the softmax-normalised output over its tokens and the log-sum-exp of its
+ * scaled logits.  Arguments as paged_decode_attention, plus:
+ *
+ *   partition_size  tokens per partition: a positive multiple of 16
+ *   tmp_out       fp32 [B][Hq][S][D], S = paged_decode_num_partitions()
+ *   tmp_lse       fp32 [B][Hq][S], natural-log LSE of the scaled logits
+ * Only partitions p < ceil(context_lens[b] / partition_size) are written;
+ * the others are left untouched.
+ */
+int paged_decode_attention_partial(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   float scale, const float* kv_scales, int32_t partition_size,
+                                   float* tmp_out, float* tmp_lse,
+                                   const pkv_desc* desc, void* stream);
+
+/*
+ * paged_decode_attention_reduce - split-context second half: merges each
+ * (sequence, query head)'s partitions p < ceil(context_lens[b] /
+ * partition_size) by out = sum_p w_p o_p / sum_p w_p, w_p = exp(lse_p -
+ * max lse).  tmp_out, tmp_lse, context_lens, partition_size and desc as
+ * given to the partial call; out [B][Hq][D] in out_dtype.
+ */
+int paged_decode_attention_reduce(const float* tmp_out, const float* tmp_lse,
+                                  const int32_t* context_lens, int32_t partition_size,
+                                  void* out, const pkv_desc* desc, void* stream);
+
+/* S = ceil(MBPS * 16 / partition_size), or -1 on invalid arguments.  */
+int64_t paged_decode_num_partitions(const pkv_desc* desc, int32_t partition_size);
+
+/* Bytes of tmp_out plus tmp_lse for the partial/reduce pair, or -1.  */
+int64_t paged_decode_workspace_bytes(const pkv_desc* desc, int32_t partition_size);
+
+/* Message of the last error on the calling thread ("" if none).  */
+const char* pkv_last_error(void);
+
+/* Library version string.  */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */

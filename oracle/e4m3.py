@@ -105,20 +105,13 @@ def quantize_blocks(x_blocks: np.ndarray, valid_tokens: np.ndarray):
     """
     x_blocks = np.asarray(x_blocks, dtype=np.float32)
     n, bs, hkv, d = x_blocks.shape
-    valid_tokens = np.asarray(valid_tokens, dtype=np.int64)
-    codes = np.zeros((n, bs, hkv, d), dtype=np.uint8)
-    scales = np.ones((n, hkv), dtype=np.float32)
-    for i in range(n):
-        nv = int(valid_tokens[i])
-        if nv <= 0:
-            continue
-        for h in range(hkv):
-            vals = x_blocks[i, :nv, h, :]
-            amax = np.float32(np.max(np.abs(vals)))
-            s = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
-            scales[i, h] = s
-            scaled = (vals / s).astype(np.float32)  # fp32 division, correctly rounded
-            codes[i, :nv, h, :] = encode(np.clip(scaled.astype(np.float64), -E4M3_MAX, E4M3_MAX))
+    valid = np.arange(bs)[None, :] < np.asarray(valid_tokens, dtype=np.int64)[:, None]   # [n, 16]
+    vals = np.where(valid[:, :, None, None], x_blocks, np.float32(0))
+    amax = np.max(np.abs(vals), axis=(1, 3)).astype(np.float32)                          # [n, Hkv]
+    scales = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1)).astype(np.float32)
+    scaled = (x_blocks / scales[:, None, :, None]).astype(np.float32)  # fp32 division, correctly rounded
+    codes = encode(np.clip(scaled.astype(np.float64), -E4M3_MAX, E4M3_MAX))
+    codes[~valid] = 0
     return codes, scales
 
 

@@ -107,12 +107,14 @@ def kv_cache_write(k_cache, v_cache, k_raw, v_raw, slot_mapping, dtype: str) -> 
     head_dim = k_raw.shape[-1]
     kidx = k_tile_index(head_dim, dtype)
     vidx = v_tile_index(head_dim, dtype)
-    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
-        if slot < 0:
-            continue
-        blk, off = int(slot) // BLOCK_SIZE, int(slot) % BLOCK_SIZE
-        k_cache[blk][:, kidx[off]] = k_raw[t]
-        v_cache[blk][:, vidx[off]] = v_raw[t]
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    keep = slots >= 0
+    slots = slots[keep]
+    blk = slots // BLOCK_SIZE                      # [T] physical block
+    off = slots % BLOCK_SIZE                       # [T] slot inside it
+    heads = np.arange(k_cache.shape[1])[None, :, None]
+    k_cache[blk[:, None, None], heads, kidx[off][:, None, :]] = np.asarray(k_raw)[keep]
+    v_cache[blk[:, None, None], heads, vidx[off][:, None, :]] = np.asarray(v_raw)[keep]
 
 
 def kv_cache_write_e4m3_blocks(k_cache, v_cache, kv_scales, k_blocks, v_blocks,
@@ -125,16 +127,24 @@ def kv_cache_write_e4m3_blocks(k_cache, v_cache, kv_scales, k_blocks, v_blocks,
     1 = V).  Slots at or past ``valid_tokens`` receive code 0.
     """
     head_dim = k_blocks.shape[-1]
-    kidx = k_tile_index(head_dim, "e4m3")
-    vidx = v_tile_index(head_dim, "e4m3")
-    kc, ks = e4m3.quantize_blocks(k_blocks, valid_tokens)
-    vc, vs = e4m3.quantize_blocks(v_blocks, valid_tokens)
-    for i, blk in enumerate(np.asarray(block_ids, dtype=np.int64)):
-        for t in range(BLOCK_SIZE):
-            k_cache[blk][:, kidx[t]] = kc[i, t]
-            v_cache[blk][:, vidx[t]] = vc[i, t]
-        kv_scales[0, blk] = ks[i]
-        kv_scales[1, blk] = vs[i]
+    n, _, hkv, _ = k_blocks.shape
+    kidx = k_tile_index(head_dim, "e4m3").ravel()   # (t, d) order
+    vidx = v_tile_index(head_dim, "e4m3").ravel()
+    ids = np.asarray(block_ids, dtype=np.int64)
+    chunk = 2048                                   # bounds the float64 temporaries
+    for c0 in range(0, n, chunk):
+        sl = slice(c0, min(n, c0 + chunk))
+        kc, ks = e4m3.quantize_blocks(k_blocks[sl], valid_tokens[sl])
+        vc, vs = e4m3.quantize_blocks(v_blocks[sl], valid_tokens[sl])
+        m = kc.shape[0]
+        ktile = np.empty((m, hkv, BLOCK_SIZE * head_dim), dtype=np.uint8)
+        vtile = np.empty_like(ktile)
+        ktile[:, :, kidx] = kc.transpose(0, 2, 1, 3).reshape(m, hkv, -1)
+        vtile[:, :, vidx] = vc.transpose(0, 2, 1, 3).reshape(m, hkv, -1)
+        k_cache[ids[sl]] = ktile
+        v_cache[ids[sl]] = vtile
+        kv_scales[0, ids[sl]] = ks
+        kv_scales[1, ids[sl]] = vs
 
 
 # ---------------------------------------------------------------- gather ---

@@ -1,0 +1,252 @@
+// abi.hip - the C ABI of libpagedkv.so (declared in include/pagedkv.h).
+//
+// Host side only: argument validation, parameter blocks, dispatch to the
+// gfx950 kernels on the caller's stream.  No allocation, no synchronisation,
+// no device reads.  Errors return a status and leave a thread-local message.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/pagedkv.h"
+#include "pkv_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return PKV_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int elem_bytes(int dt) {
+  switch (dt) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+    case PKV_E4M3: return 1;
+  }
+  return 0;
+}
+
+// Checks shared by every entry point that reads the pool.
+int check_desc(const pkv_desc* d, bool need_seqs) {
+  if (!d) return fail(PKV_ERR_INVALID_ARG, "desc is NULL");
+  if (d->num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs < 0");
+  if (need_seqs && d->num_seqs > 65535) return fail(PKV_ERR_INVALID_ARG, "num_seqs > 65535");
+  if (d->num_kv_heads < 1 || d->num_q_heads < 1)
+    return fail(PKV_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (d->num_q_heads % d->num_kv_heads)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->num_kv_heads > 65535) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads > 65535");
+  if (d->block_size != 16) return fail(PKV_ERR_INVALID_ARG, "block_size must be 16 (got %d)", d->block_size);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", d->head_dim);
+  if (d->num_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "num_blocks < 1");
+  if (d->max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq < 1");
+  if (static_cast<int64_t>(d->max_blocks_per_seq) * 16 > (int64_t(1) << 30))
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq too large");
+  return PKV_OK;
+}
+
+int check_attn_types(const pkv_desc* d, const float* kv_scales) {
+  const int q = d->q_dtype, kv = d->kv_dtype, o = d->out_dtype;
+  bool okc = false;
+  if (q == PKV_F32 && kv == PKV_F32) okc = (o == PKV_F32);
+  else if (q == PKV_F16 && kv == PKV_F16) okc = (o == PKV_F32 || o == PKV_F16);
+  else if (q == PKV_BF16 && kv == PKV_BF16) okc = (o == PKV_F32 || o == PKV_BF16);
+  else if (q == PKV_F16 && kv == PKV_E4M3) okc = (o == PKV_F32 || o == PKV_F16);
+  if (!okc) return fail(PKV_ERR_UNSUPPORTED, "unsupported dtypes q=%d kv=%d out=%d", q, kv, o);
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G > 16) return fail(PKV_ERR_UNSUPPORTED, "query heads per KV head %d > 16", G);
+  if (kv == PKV_E4M3 && !kv_scales) return fail(PKV_ERR_INVALID_ARG, "e4m3 cache needs kv_scales");
+  if (kv != PKV_E4M3 && kv_scales) return fail(PKV_ERR_INVALID_ARG, "kv_scales given for a non-e4m3 cache");
+  return PKV_OK;
+}
+
+int64_t partitions(const pkv_desc* d, int32_t psize) {
+  return (static_cast<int64_t>(d->max_blocks_per_seq) * 16 + psize - 1) / psize;
+}
+
+int check_partition(int32_t psize) {
+  if (psize <= 0 || psize % 16) return fail(PKV_ERR_INVALID_ARG, "partition_size %d is not a positive multiple of 16", psize);
+  return PKV_OK;
+}
+
+pkv::DecodeParams decode_params(const void* q, const void* kc, const void* vc, const int32_t* bt,
+                                const int32_t* cl, float scale, const float* kvs, const pkv_desc* d) {
+  pkv::DecodeParams p{};
+  p.q = q;
+  p.k_cache = kc;
+  p.v_cache = vc;
+  p.block_tables = bt;
+  p.context_lens = cl;
+  p.kv_scales = kvs;
+  p.qk_scale_log2 = scale * 1.4426950408889634f;
+  p.num_seqs = d->num_seqs;
+  p.num_q_heads = d->num_q_heads;
+  p.num_kv_heads = d->num_kv_heads;
+  p.group = d->num_q_heads / d->num_kv_heads;
+  p.num_blocks = d->num_blocks;
+  p.mbps = d->max_blocks_per_seq;
+  p.out_dtype = d->out_dtype;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err; }
+
+const char* pkv_version(void) { return "pagedkv 0.1.0 gfx950"; }
+
+int64_t paged_decode_num_partitions(const pkv_desc* desc, int32_t partition_size) {
+  if (check_desc(desc, false) || check_partition(partition_size)) return -1;
+  return partitions(desc, partition_size);
+}
+
+int64_t paged_decode_workspace_bytes(const pkv_desc* desc, int32_t partition_size) {
+  if (check_desc(desc, false) || check_partition(partition_size)) return -1;
+  const int64_t s = partitions(desc, partition_size);
+  const int64_t rows = static_cast<int64_t>(desc->num_seqs) * desc->num_q_heads * s;
+  return rows * desc->head_dim * 4 + rows * 4;
+}
+
+int kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
+                   void* k_cache, void* v_cache, const pkv_desc* desc, void* stream) {
+  if (int e = check_desc(desc, false)) return e;
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens < 0");
+  if (desc->kv_dtype == PKV_E4M3)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write into an e4m3 cache: use kv_cache_quantize_e4m3");
+  if (desc->kv_dtype != PKV_F32 && desc->kv_dtype != PKV_F16 && desc->kv_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_dtype %d", desc->kv_dtype);
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (num_tokens * desc->num_kv_heads * (desc->head_dim / 4) > (int64_t(1) << 36))
+    return fail(PKV_ERR_INVALID_ARG, "num_tokens too large");
+  pkv::WriteParams p{};
+  p.k = k;
+  p.v = v;
+  p.slots = slot_mapping;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = desc->num_kv_heads;
+  p.head_dim = desc->head_dim;
+  p.num_blocks = desc->num_blocks;
+  p.elem_bytes = elem_bytes(desc->kv_dtype);
+  return hip_status(pkv::launch_kv_write(p, static_cast<hipStream_t>(stream)), "kv_cache_write launch");
+}
+
+int kv_cache_quantize_e4m3(const float* k_src, const float* v_src, const int32_t* block_ids,
+                           const int32_t* valid_tokens, int32_t num_src_blocks, void* k_cache,
+                           void* v_cache, float* kv_scales, const pkv_desc* desc, void* stream) {
+  if (int e = check_desc(desc, false)) return e;
+  if (desc->kv_dtype != PKV_E4M3) return fail(PKV_ERR_INVALID_ARG, "kv_dtype must be e4m3");
+  if (num_src_blocks < 0 || num_src_blocks > 0x7FFFFFFF / 2)
+    return fail(PKV_ERR_INVALID_ARG, "num_src_blocks out of range");
+  if (num_src_blocks == 0) return ok();
+  if (!k_src || !v_src || !block_ids || !valid_tokens || !k_cache || !v_cache || !kv_scales)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  pkv::QuantParams p{};
+  p.k_src = k_src;
+  p.v_src = v_src;
+  p.block_ids = block_ids;
+  p.valid_tokens = valid_tokens;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.kv_scales = kv_scales;
+  p.num_src_blocks = num_src_blocks;
+  p.num_kv_heads = desc->num_kv_heads;
+  p.head_dim = desc->head_dim;
+  p.num_blocks = desc->num_blocks;
+  return hip_status(pkv::launch_quantize_e4m3(p, static_cast<hipStream_t>(stream)),
+                    "kv_cache_quantize_e4m3 launch");
+}
+
+int paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, float scale,
+                           const float* kv_scales, void* out, const pkv_desc* desc, void* stream) {
+  if (int e = check_desc(desc, true)) return e;
+  if (int e = check_attn_types(desc, kv_scales)) return e;
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  if (desc->num_seqs == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  pkv::DecodeParams p = decode_params(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales, desc);
+  p.out = out;
+  p.partition_blocks = desc->max_blocks_per_seq;
+  p.num_partitions = 1;
+  return hip_status(pkv::launch_decode(p, desc->kv_dtype, desc->head_dim, false,
+                                       static_cast<hipStream_t>(stream)),
+                    "paged_decode_attention launch");
+}
+
+int paged_decode_attention_partial(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   float scale, const float* kv_scales, int32_t partition_size,
+                                   float* tmp_out, float* tmp_lse, const pkv_desc* desc, void* stream) {
+  if (int e = check_desc(desc, true)) return e;
+  if (int e = check_attn_types(desc, kv_scales)) return e;
+  if (int e = check_partition(partition_size)) return e;
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  if (desc->num_seqs == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !tmp_out || !tmp_lse)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  const int64_t s = partitions(desc, partition_size);
+  if (s > 0x7FFFFFFF) return fail(PKV_ERR_INVALID_ARG, "too many partitions");
+  pkv::DecodeParams p = decode_params(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales, desc);
+  p.tmp_out = tmp_out;
+  p.tmp_lse = tmp_lse;
+  p.partition_blocks = partition_size / 16;
+  p.num_partitions = static_cast<int32_t>(s);
+  return hip_status(pkv::launch_decode(p, desc->kv_dtype, desc->head_dim, true,
+                                       static_cast<hipStream_t>(stream)),
+                    "paged_decode_attention_partial launch");
+}
+
+int paged_decode_attention_reduce(const float* tmp_out, const float* tmp_lse,
+                                  const int32_t* context_lens, int32_t partition_size, void* out,
+                                  const pkv_desc* desc, void* stream) {
+  if (int e = check_desc(desc, false)) return e;
+  if (int e = check_partition(partition_size)) return e;
+  const int o = desc->out_dtype;
+  if (o != PKV_F32 && o != PKV_F16 && o != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "out_dtype %d", o);
+  if (desc->num_seqs == 0) return ok();
+  if (!tmp_out || !tmp_lse || !context_lens || !out) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (static_cast<int64_t>(desc->num_seqs) * desc->num_q_heads > 0x7FFFFFFF / 2)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs * num_q_heads too large");
+  pkv::ReduceParams p{};
+  p.tmp_out = tmp_out;
+  p.tmp_lse = tmp_lse;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.num_seqs = desc->num_seqs;
+  p.num_q_heads = desc->num_q_heads;
+  p.head_dim = desc->head_dim;
+  p.mbps = desc->max_blocks_per_seq;
+  p.partition_size = partition_size;
+  p.num_partitions = static_cast<int32_t>(partitions(desc, partition_size));
+  p.out_dtype = o;
+  return hip_status(pkv::launch_reduce(p, static_cast<hipStream_t>(stream)),
+                    "paged_decode_attention_reduce launch");
+}
+
+}  // extern "C"

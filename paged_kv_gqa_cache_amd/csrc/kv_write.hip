@@ -1,0 +1,145 @@
+// kv_write.hip - moving new K/V into the paged pool (gfx950).
+//
+//  * kv_write_kernel: the step's new tokens, bit-exact, into their slots
+//    ("rvLLM: High-performance LLM inference in Rust", section "CUDA
+//    Kernels", row "Reshape and Cache"; "rvllm - A Small LLM Inference Engine
+//    in Rust", section "How it's put together": explicit write positions).
+//  * quantize_e4m3_kernel: whole blocks of fp32 K/V into E4M3 codes with one
+//    fp32 scale per (block, kv head) ("LLM Serving Kernels", section
+//    "Projects", row 05: E4M3 storage, page scales; "rvLLM: ...", "CUDA
+//    Kernels", row "FP8 KV Cache": per-head scaling).
+//
+// Both are pure data movement plus index arithmetic; the tile layouts are
+// the ones documented in pagedkv.h.
+#include "pkv_common.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+// Element offset of (token slot t, dim d) inside a V tile, n = 4 / elem bytes.
+__device__ __forceinline__ int v_tile_elem(int t, int d, int n) {
+  return (((((d / (16 * n)) * 4 + t / 4) * 16 + d % 16) * n + (d / 16) % n) * 4 + t % 4);
+}
+
+// One thread per (token, kv head, 16-byte chunk of that head's D elements).
+// K: the chunk is also a contiguous 16 bytes of the K tile (chunk c of token
+// `off` sits at byte (c*16 + off)*16).  V: its elements scatter to their
+// V-tile positions.
+template <int E>
+__global__ __launch_bounds__(256) void kv_write_kernel(const WriteParams p) {
+  typedef typename std::conditional<E == 4, uint32_t, uint16_t>::type Elem;
+  constexpr int X = 16 / E;   // elements per chunk
+  constexpr int N = 4 / E;
+  const int chunks = p.head_dim / X;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t total = p.num_tokens * p.num_kv_heads * chunks;
+  if (gid >= total) return;
+  const int c = static_cast<int>(gid % chunks);
+  const int64_t th = gid / chunks;
+  const int h = static_cast<int>(th % p.num_kv_heads);
+  const int64_t t = th / p.num_kv_heads;
+  const int64_t slot = p.slots[t];
+  if (slot < 0 || slot >= static_cast<int64_t>(p.num_blocks) * kBlockSize) return;
+  const int64_t blk = slot / kBlockSize;
+  const int off = static_cast<int>(slot % kBlockSize);
+
+  const size_t row_bytes = static_cast<size_t>(p.head_dim) * E;
+  const size_t src = (static_cast<size_t>(t) * p.num_kv_heads + h) * row_bytes + c * 16;
+  const size_t tile = (static_cast<size_t>(blk) * p.num_kv_heads + h) * kBlockSize * row_bytes;
+
+  const u32x4 kv = ld16(static_cast<const char*>(p.k) + src);
+  st16(static_cast<char*>(p.k_cache) + tile + (static_cast<size_t>(c) * kBlockSize + off) * 16, kv);
+
+  const u32x4 vv = ld16(static_cast<const char*>(p.v) + src);
+  Elem vals[X];
+  __builtin_memcpy(vals, &vv, 16);
+  Elem* vt = reinterpret_cast<Elem*>(static_cast<char*>(p.v_cache) + tile);
+#pragma unroll
+  for (int i = 0; i < X; ++i) vt[v_tile_elem(off, c * X + i, N)] = vals[i];
+}
+
+// One workgroup (D threads) per (source block, kv head, K-or-V).  Thread i
+// produces the i-th 16-byte chunk of the destination tile:
+//   K: chunk (c, t) = 16 codes of token t, dims [16c, 16c+16);
+//   V: chunk (m, g, r) = codes of dims 64m + 16q + r (q = 0..3) for tokens
+//      4g..4g+3, byte 4q + j for token 4g + j.
+// scale = fp32(amax / 448) over the block's valid slots (1 if amax is 0);
+// code = nearest-even E4M3 of clamp(fp32(x / scale), -448, 448); slots at or
+// past valid_tokens get code 0.
+__global__ __launch_bounds__(128) void quantize_e4m3_kernel(const QuantParams p) {
+  const int i = blockIdx.x;
+  const int h = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const int tid = threadIdx.x;
+  const int D = p.head_dim;
+  const int valid = max(0, min(p.valid_tokens[i], kBlockSize));
+  const float* src = is_v ? p.v_src : p.k_src;
+  auto at = [&](int t, int d) -> float {
+    return src[((static_cast<size_t>(i) * kBlockSize + t) * p.num_kv_heads + h) * D + d];
+  };
+
+  float x[16];
+  bool ok[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    int t, d;
+    if (!is_v) {
+      t = tid % 16;
+      d = 16 * (tid / 16) + k;
+    } else {
+      const int m = tid / 64, g = (tid / 16) % 4, r = tid % 16;
+      t = 4 * g + (k % 4);
+      d = 64 * m + 16 * (k / 4) + r;
+    }
+    ok[k] = t < valid;
+    x[k] = ok[k] ? at(t, d) : 0.f;
+  }
+
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(x[k]));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  __shared__ float sm[2];
+  if ((tid & 63) == 0) sm[tid >> 6] = amax;
+  __syncthreads();
+  amax = sm[0];
+  if (blockDim.x > 64) amax = fmaxf(amax, sm[1]);
+  const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float y = fminf(fmaxf(x[k] / scale, -448.0f), 448.0f);
+    const uint32_t code = ok[k] ? f32_to_e4m3(y) : 0u;
+    w[k / 4] |= code << (8 * (k % 4));
+  }
+  const int blk = p.block_ids[i];
+  char* cache = static_cast<char*>(is_v ? p.v_cache : p.k_cache);
+  const size_t tile = (static_cast<size_t>(blk) * p.num_kv_heads + h) * kBlockSize * D;
+  size_t byte;
+  if (!is_v) byte = (static_cast<size_t>(tid / 16) * kBlockSize + tid % 16) * 16;
+  else byte = static_cast<size_t>(tid) * 16;
+  st16(cache + tile + byte, u32x4{w[0], w[1], w[2], w[3]});
+  if (tid == 0)
+    p.kv_scales[((is_v ? static_cast<size_t>(p.num_blocks) : 0) + blk) * p.num_kv_heads + h] = scale;
+}
+
+hipError_t launch_kv_write(const WriteParams& p, hipStream_t stream) {
+  const int64_t chunks = p.head_dim * p.elem_bytes / 16;
+  const int64_t total = p.num_tokens * p.num_kv_heads * chunks;
+  if (total == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((total + 255) / 256)), block(256);
+  if (p.elem_bytes == 4) hipLaunchKernelGGL(kv_write_kernel<4>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(kv_write_kernel<2>, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_e4m3(const QuantParams& p, hipStream_t stream) {
+  if (p.num_src_blocks == 0) return hipSuccess;
+  const dim3 grid(p.num_src_blocks, p.num_kv_heads, 2), block(p.head_dim);
+  hipLaunchKernelGGL(quantize_e4m3_kernel, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

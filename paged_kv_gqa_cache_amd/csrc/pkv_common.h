@@ -1,0 +1,129 @@
+// pkv_common.h - device types and small helpers shared by the gfx950 kernels.
+//
+// Internal to libpagedkv.so.  Wave64 throughout: one wavefront = 64 lanes;
+// the 16x16 matrix-core ops see a lane as (group g = lane / 16, row/column
+// r = lane % 16).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace pkv {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum KvType { KV_F32 = 0, KV_F16 = 1, KV_BF16 = 2, KV_E4M3 = 3 };
+
+constexpr int kBlockSize = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int T> struct ElemBytes;
+template <> struct ElemBytes<KV_F32> { static constexpr int value = 4; };
+template <> struct ElemBytes<KV_F16> { static constexpr int value = 2; };
+template <> struct ElemBytes<KV_BF16> { static constexpr int value = 2; };
+template <> struct ElemBytes<KV_E4M3> { static constexpr int value = 1; };
+
+template <class To, class From>
+__device__ __forceinline__ To bitcast(const From& x) {
+  static_assert(sizeof(To) == sizeof(From), "size mismatch");
+  return __builtin_bit_cast(To, x);
+}
+
+// 16-byte global load / store.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Max / sum over the four lanes that share lane % 16 (lanes r, r+16, r+32, r+48).
+__device__ __forceinline__ float max_over_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+// ------------------------------------------------------------ matrix cores
+// D(16x16, f32) += A(16xK) * B(Kx16).  Lane l supplies row l%16 of A and
+// column l%16 of B, each with its k-slots (l/16)*k_per_lane + j; it receives
+// D[4*(l/16) + j][l%16] for j = 0..3.  Since A and B share the k-slot
+// assignment, which hardware k a slot is does not change the sum.
+__device__ __forceinline__ f32x4 mma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_k32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_k16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_k4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------- E4M3
+// OCP E4M3 code -> fp16 bits whose value is the code's value times 2^-8:
+// the f16 exponent field takes the code's 4 exponent bits (bias 15 instead
+// of 7) and the mantissa its 3 bits, which maps normals and subnormals alike
+// (subnormal m*2^-9 becomes f16 subnormal m*2^-17).  Two codes per call:
+// bytes 0 and 1 of x -> halves 0 and 1 of the result.
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2_scaled(uint32_t x) {
+  return ((x & 0x80u) << 8) | ((x & 0x7Fu) << 7) | ((x & 0x8000u) << 16) | ((x & 0x7F00u) << 15);
+}
+// Four codes (bytes of x) -> four f16 (value * 2^-8).
+__device__ __forceinline__ f16x4 e4m3x4_to_f16x4_scaled(uint32_t x) {
+  u32x2 r;
+  r.x = e4m3x2_to_f16x2_scaled(x);
+  r.y = e4m3x2_to_f16x2_scaled(x >> 16);
+  return bitcast<f16x4>(r);
+}
+// Sixteen codes -> two groups of eight f16 (value * 2^-8).
+__device__ __forceinline__ void e4m3x16_to_f16x8x2_scaled(u32x4 c, f16x8& lo, f16x8& hi) {
+  u32x4 a, b;
+  a.x = e4m3x2_to_f16x2_scaled(c.x);
+  a.y = e4m3x2_to_f16x2_scaled(c.x >> 16);
+  a.z = e4m3x2_to_f16x2_scaled(c.y);
+  a.w = e4m3x2_to_f16x2_scaled(c.y >> 16);
+  b.x = e4m3x2_to_f16x2_scaled(c.z);
+  b.y = e4m3x2_to_f16x2_scaled(c.z >> 16);
+  b.z = e4m3x2_to_f16x2_scaled(c.w);
+  b.w = e4m3x2_to_f16x2_scaled(c.w >> 16);
+  lo = bitcast<f16x8>(a);
+  hi = bitcast<f16x8>(b);
+}
+
+// fp32 in [-448, 448] -> nearest OCP E4M3 code, ties to even.  Below the
+// smallest normal 2^-6 the code's mantissa is the value in units of 2^-9,
+// rounded to nearest even; above, the fp32 exponent is re-biased from 127 to
+// 7 and the 23-bit mantissa rounded to 3 bits (a carry rolls into the
+// exponent).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t mag;
+  if (a < 0.015625f) {
+    mag = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+  } else {
+    const uint32_t u = __float_as_uint(a) - (120u << 23);
+    mag = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;
+  }
+  return sign | mag;
+}
+
+}  // namespace pkv

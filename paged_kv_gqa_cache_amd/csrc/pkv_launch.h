@@ -1,0 +1,66 @@
+// pkv_launch.h - kernel parameter blocks and launchers (internal to libpagedkv.so).
+//
+// The launchers assume arguments already validated by the C ABI layer
+// (abi.hip): sizes positive, supported dtypes, head_dim / group size in
+// range, partition size a multiple of 16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct DecodeParams {
+  const void* q;               // [B][Hq][D]
+  const void* k_cache;         // [NB][Hkv][tile]
+  const void* v_cache;
+  const int32_t* block_tables; // [B][MBPS]
+  const int32_t* context_lens; // [B]
+  const float* kv_scales;      // [2][NB][Hkv] (e4m3 only)
+  void* out;                   // [B][Hq][D] (final mode)
+  float* tmp_out;              // [B][Hq][S][D] (partial mode)
+  float* tmp_lse;              // [B][Hq][S]
+  float qk_scale_log2;         // scale * log2(e)
+  int32_t num_seqs, num_q_heads, num_kv_heads, group, num_blocks, mbps;
+  int32_t partition_blocks;    // blocks per partition (final mode: covers MBPS)
+  int32_t num_partitions;      // S
+  int32_t out_dtype;
+};
+
+struct ReduceParams {
+  const float* tmp_out;
+  const float* tmp_lse;
+  const int32_t* context_lens;
+  void* out;
+  int32_t num_seqs, num_q_heads, head_dim, mbps, partition_size, num_partitions, out_dtype;
+};
+
+struct WriteParams {
+  const void* k;
+  const void* v;
+  const int64_t* slots;
+  void* k_cache;
+  void* v_cache;
+  int64_t num_tokens;
+  int32_t num_kv_heads, head_dim, num_blocks, elem_bytes;
+};
+
+struct QuantParams {
+  const float* k_src;           // [n][16][Hkv][D]
+  const float* v_src;
+  const int32_t* block_ids;     // [n]
+  const int32_t* valid_tokens;  // [n]
+  void* k_cache;
+  void* v_cache;
+  float* kv_scales;             // [2][NB][Hkv]
+  int32_t num_src_blocks, num_kv_heads, head_dim, num_blocks;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool partial,
+                         hipStream_t stream);
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
+hipError_t launch_kv_write(const WriteParams& p, hipStream_t stream);
+hipError_t launch_quantize_e4m3(const QuantParams& p, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/pagedkv.h declares, and rejects bad arguments with the
+documented status before touching the device."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from paged_kv_gqa_cache_amd import abi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pagedkv.h")
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 9, names
+    lib = ctypes.CDLL(abi.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in pagedkv.h but not exported"
+    assert set(abi.EXPORTED) == set(names)
+
+
+def test_version():
+    assert "gfx950" in abi.version()
+
+
+def desc(**kw):
+    base = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=64, num_blocks=10,
+                max_blocks_per_seq=4, q_dtype=abi.PKV_F16, kv_dtype=abi.PKV_F16, out_dtype=abi.PKV_F32)
+    block_size = kw.pop("block_size", None)
+    base.update(kw)
+    d = abi.make_desc(**base)
+    if block_size is not None:
+        d.block_size = block_size
+    return d
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation first
+
+
+def attn(d, scale=0.125, kv_scales=None, ptr=FAKE):
+    return abi.lib().paged_decode_attention(ptr, ptr, ptr, ptr, ptr, scale, kv_scales, ptr,
+                                            ctypes.byref(d), None)
+
+
+def partial(d, P, scale=0.125):
+    return abi.lib().paged_decode_attention_partial(FAKE, FAKE, FAKE, FAKE, FAKE, scale, None, P,
+                                                    FAKE, FAKE, ctypes.byref(d), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), UNSUPPORTED),
+    (dict(head_dim=256), UNSUPPORTED),
+    (dict(num_q_heads=34, num_kv_heads=2), UNSUPPORTED),          # G = 17 > 16
+    (dict(num_q_heads=9, num_kv_heads=2), INVALID),               # not a multiple
+    (dict(block_size=32), INVALID),
+    (dict(num_blocks=0), INVALID),
+    (dict(max_blocks_per_seq=0), INVALID),
+    (dict(num_seqs=-1), INVALID),
+    (dict(q_dtype=abi.PKV_BF16), UNSUPPORTED),                    # q bf16 with f16 KV
+    (dict(out_dtype=abi.PKV_BF16), UNSUPPORTED),                  # f16 path cannot emit bf16
+    (dict(q_dtype=abi.PKV_F32, kv_dtype=abi.PKV_F32, out_dtype=abi.PKV_F16), UNSUPPORTED),
+    (dict(q_dtype=abi.PKV_F16, kv_dtype=abi.PKV_E4M3), INVALID),  # e4m3 without kv_scales
+    (dict(q_dtype=7), UNSUPPORTED),
+])
+def test_attention_rejects_bad_descriptors(kw, code):
+    assert attn(desc(**kw)) == code
+    assert abi.last_error()
+
+
+def test_attention_rejects_null_pointers_and_bad_scale():
+    assert attn(desc(), ptr=None) == INVALID
+    assert "null" in abi.last_error()
+    assert attn(desc(), scale=math.inf) == INVALID
+    assert attn(desc(), scale=math.nan) == INVALID
+    scales = ctypes.c_void_p(0x2000)
+    assert attn(desc(), kv_scales=scales) == INVALID            # scales for a 16-bit cache
+
+
+def test_empty_batch_is_a_no_op():
+    assert attn(desc(num_seqs=0), ptr=None) == OK
+    assert abi.last_error() == ""
+
+
+@pytest.mark.parametrize("P", [0, -16, 8, 24, 100])
+def test_partial_rejects_bad_partition_sizes(P):
+    assert partial(desc(), P) == INVALID
+    assert "partition_size" in abi.last_error()
+
+
+def test_reduce_rejects_bad_arguments():
+    d = desc(out_dtype=abi.PKV_E4M3)
+    assert abi.lib().paged_decode_attention_reduce(FAKE, FAKE, FAKE, 64, FAKE, ctypes.byref(d), None) == UNSUPPORTED
+    d = desc()
+    assert abi.lib().paged_decode_attention_reduce(FAKE, FAKE, FAKE, 40, FAKE, ctypes.byref(d), None) == INVALID
+    assert abi.lib().paged_decode_attention_reduce(None, FAKE, FAKE, 64, FAKE, ctypes.byref(d), None) == INVALID
+
+
+def test_write_rejects_e4m3_and_bad_sizes():
+    d = desc(kv_dtype=abi.PKV_E4M3)
+    assert abi.lib().kv_cache_write(FAKE, FAKE, FAKE, 4, FAKE, FAKE, ctypes.byref(d), None) == UNSUPPORTED
+    d = desc()
+    assert abi.lib().kv_cache_write(FAKE, FAKE, FAKE, -1, FAKE, FAKE, ctypes.byref(d), None) == INVALID
+    assert abi.lib().kv_cache_write(None, FAKE, FAKE, 4, FAKE, FAKE, ctypes.byref(d), None) == INVALID
+    assert abi.lib().kv_cache_write(None, None, None, 0, None, None, ctypes.byref(d), None) == OK
+
+
+def test_quantize_requires_e4m3_cache():
+    d = desc()
+    assert abi.lib().kv_cache_quantize_e4m3(FAKE, FAKE, FAKE, FAKE, 3, FAKE, FAKE, FAKE,
+                                            ctypes.byref(d), None) == INVALID
+    d = desc(kv_dtype=abi.PKV_E4M3)
+    assert abi.lib().kv_cache_quantize_e4m3(FAKE, None, FAKE, FAKE, 3, FAKE, FAKE, FAKE,
+                                            ctypes.byref(d), None) == INVALID
+
+
+def test_partition_count_and_workspace_size():
+    d = desc(num_seqs=128, num_q_heads=28, num_kv_heads=4, head_dim=128, max_blocks_per_seq=533)
+    assert abi.lib().paged_decode_num_partitions(ctypes.byref(d), 512) == math.ceil(533 * 16 / 512)
+    S = math.ceil(533 * 16 / 512)
+    assert abi.lib().paged_decode_workspace_bytes(ctypes.byref(d), 512) == 128 * 28 * S * (128 + 1) * 4
+    assert abi.lib().paged_decode_num_partitions(ctypes.byref(d), 40) == -1
+    assert abi.num_partitions(533, 512) == S

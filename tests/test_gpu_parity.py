@@ -1,0 +1,247 @@
+"""GPU parity: the HIP library against the float64 oracle, element by element,
+on the same seeded inputs.  Gate: max |GPU - oracle| <= 2e-3 on an fp32
+output (FP8: against the oracle run on the same dequantised values); integer
+and byte work (slot write, E4M3 codes and scales) bit-exact."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import paged_attention as ref
+from paged_kv_gqa_cache_amd import workloads
+from tests.gpu_util import OUT_DT, decode, gpu_pool, inputs, to_dev, to_raw
+from tests.helpers import oracle_pool
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+# Reduced variants: several blocks per sequence, ragged last blocks, sizes the
+# oracle finishes in about a second.
+REDUCED = {
+    "tiny": dict(),
+    "smollm2_360m": dict(num_seqs=5, lengths=("uniform", 1, 700)),
+    "qwen25_1p5b": dict(num_seqs=4, lengths=("uniform", 1, 900)),
+    "qwen25_7b_prefix": dict(num_seqs=16, lengths=("lognormal", 300, 1.0, 16, 3000)),
+    "qwen25_7b_fp8": dict(num_seqs=3, lengths=("uniform", 1, 700)),
+}
+NAMES = list(REDUCED)
+
+
+def oracle_out(w, pool=None):
+    k, v, sc = pool if pool is not None else oracle_pool(w)
+    return ref.decode_attention(w.q, w.spec.q_dtype, k, v, w.spec.kv_dtype, w.block_tables,
+                                w.context_lens, w.scale, sc)
+
+
+def max_err(got: torch.Tensor, want: np.ndarray) -> float:
+    g = got.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(g)), "non-finite output"
+    return float(np.max(np.abs(g - want))) if want.size else 0.0
+
+
+def _announce(*what):
+    print("case:", *what, flush=True)
+
+
+@pytest.mark.parametrize("name", NAMES)
+@pytest.mark.parametrize("mode", ["single", "split"])
+def test_decode_matches_oracle(name, mode):
+    _announce(name, mode)
+    w = workloads.generate(name, **REDUCED[name])
+    want = oracle_out(w)
+    got = decode(w, gpu_pool(w), mode)
+    assert max_err(got, want) <= TOL
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", dict(num_q_heads=4, num_kv_heads=4, num_seqs=3)),                 # G = 1 (MHA)
+    ("tiny", dict(num_q_heads=16, num_kv_heads=1, num_seqs=3)),                # G = 16 (MQA)
+    ("smollm2_360m", dict(num_seqs=3, head_dim=128, lengths=("uniform", 1, 300))),
+    ("qwen25_7b_prefix", dict(num_seqs=9, head_dim=64, lengths=("uniform", 1, 600))),
+    ("qwen25_7b_fp8", dict(num_seqs=3, head_dim=64, lengths=("uniform", 1, 500))),
+    ("qwen25_1p5b", dict(num_seqs=2, lengths=("uniform", 1, 16))),             # one block or less
+])
+@pytest.mark.parametrize("mode", ["single", "split"])
+def test_decode_shape_variants(name, kw, mode):
+    _announce(name, kw, mode)
+    w = workloads.generate(name, **kw)
+    assert max_err(decode(w, gpu_pool(w), mode, partition_size=64), oracle_out(w)) <= TOL
+
+
+@pytest.mark.parametrize("mode", ["single", "split"])
+def test_longest_context(mode):
+    """Two sequences at the 32768-token clip of the lognormal workload:
+    2048 blocks each, many 64-block id chunks per wave."""
+    _announce("longest", mode)
+    w = workloads.generate("qwen25_7b_prefix", num_seqs=2, lengths=("fixed", 32768), prefix_group=0)
+    assert max_err(decode(w, gpu_pool(w), mode), oracle_out(w)) <= TOL
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen25_1p5b", "smollm2_360m", "qwen25_7b_prefix"])
+def test_kv_cache_write_is_bit_exact(name):
+    _announce("write", name)
+    w = workloads.generate(name, **REDUCED[name])
+    k_o, v_o, _ = oracle_pool(w)
+    k_g, v_g, _ = gpu_pool(w)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_raw(k_g, w.spec.kv_dtype), k_o)
+    assert np.array_equal(to_raw(v_g, w.spec.kv_dtype), v_o)
+
+
+@pytest.mark.parametrize("kw", [dict(num_seqs=3, lengths=("uniform", 1, 700)),
+                                dict(num_seqs=2, lengths=("uniform", 1, 300), head_dim=64)])
+def test_quantize_e4m3_is_bit_exact(kw):
+    _announce("quantize", kw)
+    w = workloads.generate("qwen25_7b_fp8", **kw)
+    k_o, v_o, s_o = oracle_pool(w)
+    k_g, v_g, s_g = gpu_pool(w)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_raw(k_g, "e4m3"), k_o)
+    assert np.array_equal(to_raw(v_g, "e4m3"), v_o)
+    assert np.array_equal(s_g.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+
+
+def test_fp8_attention_on_oracle_codes():
+    """The FP8 kernel fed the oracle's own codes and scales (uploaded)."""
+    _announce("fp8 oracle codes")
+    w = workloads.generate("qwen25_7b_fp8", num_seqs=3, lengths=("uniform", 100, 700))
+    k_o, v_o, s_o = oracle_pool(w)
+    pool = (to_dev(k_o, "e4m3"), to_dev(v_o, "e4m3"), torch.from_numpy(s_o).cuda())
+    want = oracle_out(w, (k_o, v_o, s_o))
+    for mode in ("single", "split"):
+        assert max_err(decode(w, pool, mode), want) <= TOL
+
+
+@pytest.mark.parametrize("P", [16, 64, 256, 2048])
+def test_partials_match_oracle_partials(P):
+    _announce("partials", P)
+    w = workloads.generate("qwen25_7b_prefix", num_seqs=6, lengths=("uniform", 1, 2500))
+    k, v, sc = oracle_pool(w)
+    from paged_kv_gqa_cache_amd import abi
+    pool = gpu_pool(w)
+    q, tables, lens = inputs(w)
+    tmp_out, tmp_lse = abi.alloc_partials(q, tables.shape[1], P)
+    tmp_out.fill_(float("nan"))
+    tmp_lse.fill_(float("nan"))
+    abi.paged_decode_attention_partial(q, pool[0], pool[1], tables, lens, w.scale, None, P, tmp_out, tmp_lse)
+    S = tmp_out.shape[2]
+    o_ref, lse_ref = ref.decode_partials(w.q, "bf16", k, v, "bf16", w.block_tables, w.context_lens,
+                                         w.scale, P, S)
+    o_g, lse_g = tmp_out.cpu().numpy(), tmp_lse.cpu().numpy()
+    for b, L in enumerate(w.context_lens):
+        n = ref.num_partitions(L, P)
+        assert np.max(np.abs(o_g[b, :, :n] - o_ref[b, :, :n])) <= TOL
+        assert np.max(np.abs(lse_g[b, :, :n] - lse_ref[b, :, :n])) <= TOL
+        assert np.all(np.isnan(o_g[b, :, n:])) and np.all(np.isnan(lse_g[b, :, n:])), "wrote past its partitions"
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    abi.paged_decode_attention_reduce(tmp_out, tmp_lse, lens, P, out, tables.shape[1])
+    assert max_err(out, ref.merge_partials(o_ref, lse_ref, w.context_lens, P)) <= TOL
+
+
+def test_partition_sizes_agree():
+    _announce("partition sweep")
+    w = workloads.generate("qwen25_1p5b", num_seqs=4, lengths=("uniform", 1, 3000))
+    want = oracle_out(w)
+    pool = gpu_pool(w)
+    for P in (16, 64, 512, 2048, 16 * w.max_blocks_per_seq):
+        assert max_err(decode(w, pool, "split", partition_size=P), want) <= TOL, P
+
+
+@pytest.mark.parametrize("name", ["qwen25_1p5b", "qwen25_7b_prefix", "qwen25_7b_fp8"])
+@pytest.mark.parametrize("mode", ["single", "split"])
+def test_out_in_query_dtype_is_fp32_out_rounded(name, mode):
+    _announce("out dtype", name, mode)
+    w = workloads.generate(name, **REDUCED[name])
+    pool = gpu_pool(w)
+    odt = OUT_DT[w.spec.q_dtype]
+    o32 = decode(w, pool, mode, out_dtype=torch.float32)
+    o16 = decode(w, pool, mode, out_dtype=odt)
+    rounded = o32.to(odt)
+    # within one unit in the last place of the 16-bit type
+    ulp = (rounded.float().abs() * (2.0 ** -10 if odt == torch.float16 else 2.0 ** -7)).clamp_min(1e-30)
+    assert torch.all((o16.float() - rounded.float()).abs() <= ulp)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen25_1p5b"])
+@pytest.mark.parametrize("mode", ["single", "split"])
+def test_context_len_one_returns_the_new_v(name, mode):
+    _announce("L=1", name, mode)
+    w = workloads.generate(name, num_seqs=5, lengths=("fixed", 1))
+    got = decode(w, gpu_pool(w), mode).cpu().numpy()
+    s = w.spec
+    v = ref.to_f64(w.new_v, s.kv_dtype)
+    for b in range(s.num_seqs):
+        for i in range(s.num_q_heads):
+            assert np.array_equal(got[b, i].astype(np.float64), v[b, i // s.group_size])
+
+
+def test_block_relabelling_is_bitwise_invariant():
+    _announce("relabel")
+    w = workloads.generate("qwen25_7b_prefix", num_seqs=12, lengths=("uniform", 1, 800))
+    k, v, _ = gpu_pool(w)
+    base = decode(w, (k, v, None), "split")
+    perm = torch.from_numpy(np.random.default_rng(9).permutation(w.num_blocks)).cuda()
+    k2, v2 = torch.empty_like(k), torch.empty_like(v)
+    k2[perm], v2[perm] = k, v
+    t = torch.from_numpy(w.block_tables).cuda().long()
+    t2 = torch.where(t >= 0, perm[t.clamp_min(0)], t).int()
+    out = decode(w, (k2, v2, None), "split", tables=t2)
+    assert torch.equal(out, base)
+
+
+def test_equal_queries_in_a_group_are_bitwise_equal():
+    _announce("gqa equal")
+    w = workloads.generate("qwen25_7b_prefix", num_seqs=6, lengths=("uniform", 1, 800))
+    q, _, _ = inputs(w)
+    G = w.spec.group_size
+    q = q.view(q.shape[0], -1, G, q.shape[2])[:, :, :1].expand(-1, -1, G, -1).reshape(q.shape).contiguous()
+    out = decode(w, gpu_pool(w), "split", q=q)
+    o = out.view(out.shape[0], -1, G, out.shape[2])
+    assert torch.equal(o, o[:, :, :1].expand_as(o))
+
+
+@pytest.mark.parametrize("mode", ["single", "split"])
+def test_empty_context_gives_zeros(mode):
+    _announce("empty", mode)
+    w = workloads.generate("qwen25_1p5b", num_seqs=4, lengths=("uniform", 20, 200))
+    lens = torch.from_numpy(w.context_lens).cuda()
+    lens[2] = 0
+    got = decode(w, gpu_pool(w), mode, lens=lens)
+    want = ref.decode_attention(w.q, "f16", *oracle_pool(w)[:2], "f16", w.block_tables,
+                                lens.cpu().numpy(), w.scale)
+    assert torch.all(got[2] == 0)
+    assert max_err(got, want) <= TOL
+
+
+# ------------------------------------------------------- full-size configs ---
+
+FULL_SAMPLE = 6
+
+
+@pytest.mark.parametrize("name", ["smollm2_360m", "qwen25_1p5b", "qwen25_7b_prefix", "qwen25_7b_fp8"])
+def test_full_size_sampled_sequences(name):
+    """Each workload at its full size, in the split configuration the benchmark
+    times; the oracle checks a sample of sequences (the longest, the shortest
+    and random others)."""
+    _announce("full", name)
+    w = workloads.generate(name)
+    got = decode(w, gpu_pool(w), "split").cpu().numpy()
+    L = w.context_lens
+    rng = np.random.default_rng(0)
+    pick = {int(np.argmax(L)), int(np.argmin(L))}
+    pick |= set(rng.choice(len(L), size=FULL_SAMPLE, replace=False).tolist())
+    pick = sorted(pick)[:FULL_SAMPLE + 2]
+    # the oracle builds only the blocks the sampled sequences read
+    used = np.unique(w.block_tables[pick][w.block_tables[pick] >= 0])
+    keep = np.isin(w.fill_blocks, used)
+    sub = workloads.Workload(**{**w.__dict__})
+    sub.fill_blocks, sub.fill_valid = w.fill_blocks[keep], w.fill_valid[keep]
+    sub.fill_k, sub.fill_v = w.fill_k[keep], w.fill_v[keep]
+    sub.q = w.q[pick]
+    sub.block_tables = w.block_tables[pick]
+    sub.context_lens = w.context_lens[pick]
+    want = oracle_out(sub)
+    assert float(np.max(np.abs(got[pick] - want))) <= TOL
+    assert np.all(np.isfinite(got))
