@@ -1,0 +1,303 @@
+"""Benchmark: paged GQA decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one decode-attention step of one layer for the whole batch: the
+new-token slot write (for workloads that have one), the split-context
+partial kernel and the LSE merge kernel, all through the C ABI.  Each step
+uses the next of several layer pools in turn (distinct HBM buffers, more
+bytes than the 256 MB Infinity Cache holds), as consecutive layers of a real
+decode step do, so every step reads its K/V from HBM.
+
+Prints ONE JSON line.  ``value`` is the headline workload's K/V-read
+throughput: unique K/V bytes per step (each physical (block, kv head) tile
+counted once, by the tokens read from it) over the wall time per step.
+``roofline`` rates the partial kernel alone: the same bytes over its average
+duration, measured inside the timed region with HIP events recorded on the
+stream the kernel runs on (events created with hipEventDisableSystemFence,
+which costs about 1 us per step instead of about 5).  ``cpu_baseline`` is the
+float64 oracle on the host, one thread, on the same batch.  A second workload
+(the B=32 Qwen2.5-1.5B-shaped layer with its new-token write) is timed in the
+same run and reported as ``b32``.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+HEADLINE = "qwen25_7b_prefix"
+SECONDARY = "qwen25_1p5b"
+
+DESCRIPTIONS = {
+    "qwen25_7b_prefix": "Qwen2.5-7B-shaped attention layer: 128 seqs, 28 Q / 4 KV heads, head_dim 128, "
+                        "bf16 q/K/V, 16-token blocks, lognormal context (median 1024, sigma 1, clip "
+                        "[16, 32768]), 8-seq groups share 32 prefix blocks, split-context partitions",
+    "qwen25_1p5b": "Qwen2.5-1.5B-shaped attention layer: 32 seqs, 12 Q / 2 KV heads, head_dim 128, "
+                   "fp16, 16-token blocks, context uniform [512, 4096], new-token write of 32 tokens",
+    "smollm2_360m": "SmolLM2-360M-shaped attention layer: 16 seqs, 15 Q / 5 KV heads, head_dim 64, fp16",
+    "qwen25_7b_fp8": "Qwen2.5-7B-shaped attention layer, FP8 E4M3 KV with per-(block, kv head) scales: "
+                     "64 seqs, 28 Q / 4 KV heads, head_dim 128, context 8192, q fp16",
+    "tiny": "4 seqs, 8 Q / 2 KV heads, head_dim 64, fp32, pool of 128 blocks",
+}
+DTYPE_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16", "e4m3": "e4m3"}
+
+
+class HipEvents:
+    """Timing events on a given stream, straight from the HIP runtime."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n: int):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+            self.ev.append(e)
+
+    def record(self, i: int, stream_handle: int) -> None:
+        self.hip.hipEventRecord(self.ev[i], self.ct.c_void_p(stream_handle))
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        f = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(f), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return f.value
+
+    def close(self) -> None:
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_gqa_cache_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_traffic(workload: str, digest: str):
+    """HBM bytes per partial-kernel launch from the committed rocprofv3 counter
+    summary, if it was taken from the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"paged_decode_partial_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_digest") != digest:
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_dispatch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+class Runner:
+    """Device state for one workload: layer pools, inputs, workspace."""
+
+    def __init__(self, name: str, layers: int, partition_size=None, path: str = "pair"):
+        import torch
+        from paged_kv_gqa_cache_amd import abi, workloads
+        from tests.gpu_util import gpu_pool, inputs, to_dev
+
+        self.torch, self.abi = torch, abi
+        self.w = w = workloads.generate(name)
+        self.spec = s = w.spec
+        self.P = partition_size or s.partition_size
+        base = gpu_pool(w, with_new_tokens=False)
+        self.pools = [base] + [tuple(None if t is None else t.clone() for t in base) for _ in range(layers - 1)]
+        self.q, self.tables, self.lens = inputs(w)
+        self.tmp_out, self.tmp_lse = abi.alloc_partials(self.q, self.tables.shape[1], self.P)
+        self.ws = abi.split_workspace(self.q, base[0], self.tables, self.P)
+        self.path = path
+        self.out = torch.empty(self.q.shape, dtype={"f32": torch.float32, "f16": torch.float16,
+                                                    "bf16": torch.bfloat16}[s.q_dtype], device="cuda")
+        self.new = None
+        if w.new_slots is not None:
+            self.new = (to_dev(w.new_k, s.kv_dtype), to_dev(w.new_v, s.kv_dtype),
+                        torch.from_numpy(w.new_slots).cuda())
+        self.unique_bytes = workloads.kv_bytes(w, unique=True)
+        self.logical_bytes = workloads.kv_bytes(w, unique=False)
+        torch.cuda.synchronize()
+
+    def step(self, i: int, ev=None, e0: int = 0) -> None:
+        """One decode step on layer pool i % layers; with ``ev``, events e0 and
+        e0 + 1 bracket the dominant kernel (the partial or the fused split)."""
+        abi = self.abi
+        k, v, sc = self.pools[i % len(self.pools)]
+        stream = self.torch.cuda.current_stream().cuda_stream
+        if self.new is not None:
+            abi.kv_cache_write(self.new[0], self.new[1], self.new[2], k, v)
+        if ev is not None:
+            ev.record(e0, stream)
+        if self.path == "fused":
+            abi.paged_decode_attention_split(self.q, k, v, self.tables, self.lens, self.w.scale, sc,
+                                             self.P, self.ws, out=self.out)
+            if ev is not None:
+                ev.record(e0 + 1, stream)
+        else:
+            abi.paged_decode_attention_partial(self.q, k, v, self.tables, self.lens, self.w.scale, sc,
+                                               self.P, self.tmp_out, self.tmp_lse)
+            if ev is not None:
+                ev.record(e0 + 1, stream)
+            abi.paged_decode_attention_reduce(self.tmp_out, self.tmp_lse, self.lens, self.P, self.out,
+                                              self.tables.shape[1])
+
+    def run(self, steps: int, warmup: int):
+        """Returns (seconds per step, [dominant-kernel ms per step])."""
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        ev = HipEvents(2 * steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(warmup + i, ev, 2 * i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kernel_ms = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)]
+        ev.close()
+        return wall / steps, kernel_ms
+
+
+def cpu_baseline(name: str):
+    """The float64 oracle on this host, one thread, on the full batch."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged_attention as ref
+    from paged_kv_gqa_cache_amd import workloads
+    from tests.helpers import oracle_pool
+
+    w = workloads.generate(name)
+    k, v, sc = oracle_pool(w)
+    s = w.spec
+    times = []
+    with threadpool_limits(1):
+        for _ in range(2):
+            t = time.perf_counter()
+            if w.new_slots is not None:
+                ref.kv_cache_write(k, v, w.new_k, w.new_v, w.new_slots, s.kv_dtype)
+            ref.decode_attention(w.q, s.q_dtype, k, v, s.kv_dtype, w.block_tables, w.context_lens,
+                                 w.scale, sc)
+            times.append(time.perf_counter() - t)
+    t = min(times)
+    return {"value": round(workloads.kv_bytes(w, unique=True) / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the full {s.num_seqs}-sequence batch of the headline workload, one decode step "
+                      f"(gather + softmax + PV in float64, numpy, 1 BLAS thread); best of 2 runs: "
+                      f"{t * 1e3:.0f} ms per step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=4, help="layer pools rotated through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--path", choices=["pair", "fused"], default="pair",
+                    help="partial + reduce kernels, or the one-launch split with in-kernel merge")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 256 MiB device to device (reference kernel for HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_gqa_cache_amd import abi
+
+    torch.cuda.set_device(0)
+    digest = source_digest()
+    if args.copy_calibration:
+        a = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        torch.empty_like(a).copy_(a)
+        torch.cuda.synchronize()
+        del a
+
+    r = Runner(args.workload, args.layers, args.partition_size, args.path)
+    t_step, part_ms = r.run(args.steps, args.warmup)
+    part_avg = sum(part_ms) / len(part_ms)
+    value = r.unique_bytes / t_step / 1e9
+    achieved = r.unique_bytes / (part_avg * 1e-3) / 1e9
+    s = r.spec
+
+    b32 = None
+    if not args.no_secondary and args.workload != SECONDARY:
+        r2 = Runner(SECONDARY, args.layers, None, args.path)
+        t2, p2 = r2.run(args.steps, args.warmup)
+        b32 = {"workload": f"{SECONDARY}: {DESCRIPTIONS[SECONDARY]}", "path": args.path,
+               "partition_size": r2.P, "us_per_step": round(t2 * 1e6, 2),
+               "dominant_kernel_us": round(sum(p2) / len(p2) * 1e3, 2),
+               "kv_GBps": round(r2.unique_bytes / t2 / 1e9, 1),
+               "seqs_layers_per_s": round(r2.spec.num_seqs / t2, 1)}
+        del r2
+
+    line = {
+        "metric": "paged GQA decode attn: KV-read HBM GB/s (% of peak) + us/step at B=32/128",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[s.kv_dtype],
+        "data": "synthetic (seeded N(0,1) q/K/V, seeded context lengths and block tables)",
+        "config": {
+            "workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",
+            "num_seqs": s.num_seqs, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
+            "head_dim": s.head_dim, "block_size": 16, "partition_size": r.P,
+            "layer_pools": args.layers, "mean_context": round(float(r.w.context_lens.mean()), 1),
+            "kv_bytes_unique": r.unique_bytes, "kv_bytes_logical": r.logical_bytes,
+        },
+        "us_per_step": round(t_step * 1e6, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 1),
+        "seqs_layers_per_s": round(s.num_seqs / t_step, 1),
+        "logical_GBps": round(r.logical_bytes / t_step / 1e9, 1),
+        "path": args.path,
+        "dominant_kernel_us": round(part_avg * 1e3, 2),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": counters_traffic(args.workload, digest),
+            "kernel": ("paged_decode_persistent, split partial mode" if args.path == "pair"
+                       else "paged_decode_persistent, split mode with in-kernel merge"),
+        },
+        "b32": b32,
+        "kernel_source_digest": digest,
+        "library": abi.version(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

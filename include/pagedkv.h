@@ -191,6 +191,33 @@ int paged_decode_attention_reduce(const float* tmp_out, const float* tmp_lse,
                                   const int32_t* context_lens, int32_t partition_size,
                                   void* out, const pkv_desc* desc, void* stream);
 
+/*
+ * paged_decode_attention_split - the partial and reduce halves in one
+ * launch: same result as paged_decode_attention_partial followed by
+ * paged_decode_attention_reduce.  A sequence whose context fits one
+ * partition writes out directly; for the others, the last partition of each
+ * (sequence, kv head) to finish merges all of them (flash-decoding with the
+ * log-sum-exp merge done in-kernel).  Arguments as the partial call, plus:
+ *
+ *   workspace        device memory of workspace_bytes >=
+ *                    paged_decode_split_workspace_bytes(desc, partition_size)
+ *                    bytes, 256-byte aligned.  It holds per-(sequence, kv
+ *                    head) int32 counters followed by the partials.  It must
+ *                    be zero-filled before its first use; every call leaves
+ *                    the counters zero again, so later calls may reuse it
+ *                    without clearing.  Calls that run at the same time must
+ *                    not share a workspace.
+ *   out              [B][Hq][D] in out_dtype
+ */
+int paged_decode_attention_split(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 float scale, const float* kv_scales, int32_t partition_size,
+                                 void* workspace, int64_t workspace_bytes, void* out,
+                                 const pkv_desc* desc, void* stream);
+
+/* Workspace bytes paged_decode_attention_split needs, or -1.  */
+int64_t paged_decode_split_workspace_bytes(const pkv_desc* desc, int32_t partition_size);
+
 /* S = ceil(MBPS * 16 / partition_size), or -1 on invalid arguments.  */
 int64_t paged_decode_num_partitions(const pkv_desc* desc, int32_t partition_size);
 

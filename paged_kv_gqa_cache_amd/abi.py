@@ -18,7 +18,7 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(_HERE, "libpagedkv.so")
 
 PKV_F32, PKV_F16, PKV_BF16, PKV_E4M3 = 0, 1, 2, 3
 _TORCH_CODE = {
@@ -54,6 +54,8 @@ def _load():
         "paged_decode_attention": (ctypes.c_int, [P, P, P, P, P, F, P, P, D, P]),
         "paged_decode_attention_partial": (ctypes.c_int, [P, P, P, P, P, F, P, I32, P, P, D, P]),
         "paged_decode_attention_reduce": (ctypes.c_int, [P, P, P, I32, P, D, P]),
+        "paged_decode_attention_split": (ctypes.c_int, [P, P, P, P, P, F, P, I32, P, I64, P, D, P]),
+        "paged_decode_split_workspace_bytes": (ctypes.c_int64, [D, I32]),
         "paged_decode_num_partitions": (ctypes.c_int64, [D, I32]),
         "paged_decode_workspace_bytes": (ctypes.c_int64, [D, I32]),
         "pkv_last_error": (ctypes.c_char_p, []),
@@ -68,6 +70,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("kv_cache_write", "kv_cache_quantize_e4m3", "paged_decode_attention",
             "paged_decode_attention_partial", "paged_decode_attention_reduce",
+            "paged_decode_attention_split", "paged_decode_split_workspace_bytes",
             "paged_decode_num_partitions", "paged_decode_workspace_bytes", "pkv_last_error",
             "pkv_version")
 
@@ -186,3 +189,24 @@ def paged_decode_attention_reduce(tmp_out, tmp_lse, context_lens, partition_size
     _check("paged_decode_attention_reduce", _lib.paged_decode_attention_reduce(
         _ptr(tmp_out), _ptr(tmp_lse), _ptr(context_lens), int(partition_size), _ptr(out),
         ctypes.byref(desc), _stream(stream)))
+
+
+def split_workspace(q, k_cache, block_tables, partition_size: int) -> torch.Tensor:
+    """A zero-filled workspace for paged_decode_attention_split (reusable across calls)."""
+    desc = _attn_desc(q, k_cache, block_tables, PKV_F32)
+    n = _lib.paged_decode_split_workspace_bytes(ctypes.byref(desc), int(partition_size))
+    if n < 0:
+        raise PkvError("paged_decode_split_workspace_bytes", 1, last_error())
+    return torch.zeros(int(n), dtype=torch.uint8, device=q.device)
+
+
+def paged_decode_attention_split(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales,
+                                 partition_size, workspace, out=None, out_dtype=None, stream=None):
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    desc = _attn_desc(q, k_cache, block_tables, _code(out))
+    _check("paged_decode_attention_split", _lib.paged_decode_attention_split(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        float(scale), _ptr(kv_scales), int(partition_size), _ptr(workspace), workspace.numel(),
+        _ptr(out), ctypes.byref(desc), _stream(stream)))
+    return out

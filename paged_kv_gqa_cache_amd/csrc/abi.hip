@@ -82,6 +82,20 @@ int64_t partitions(const pkv_desc* d, int32_t psize) {
   return (static_cast<int64_t>(d->max_blocks_per_seq) * 16 + psize - 1) / psize;
 }
 
+// Split workspace: [counters int32 B*Hkv | pad to 256][tmp_lse f32 B*Hq*S | pad][tmp_out f32 B*Hq*S*D]
+struct SplitLayout {
+  int64_t lse_off, out_off, total;
+};
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+SplitLayout split_layout(const pkv_desc* d, int64_t s) {
+  SplitLayout l;
+  const int64_t rows = static_cast<int64_t>(d->num_seqs) * d->num_q_heads * s;
+  l.lse_off = align256(static_cast<int64_t>(d->num_seqs) * d->num_kv_heads * 4);
+  l.out_off = l.lse_off + align256(rows * 4);
+  l.total = l.out_off + rows * d->head_dim * 4;
+  return l;
+}
+
 int check_partition(int32_t psize) {
   if (psize <= 0 || psize % 16) return fail(PKV_ERR_INVALID_ARG, "partition_size %d is not a positive multiple of 16", psize);
   return PKV_OK;
@@ -125,6 +139,11 @@ int64_t paged_decode_workspace_bytes(const pkv_desc* desc, int32_t partition_siz
   const int64_t s = partitions(desc, partition_size);
   const int64_t rows = static_cast<int64_t>(desc->num_seqs) * desc->num_q_heads * s;
   return rows * desc->head_dim * 4 + rows * 4;
+}
+
+int64_t paged_decode_split_workspace_bytes(const pkv_desc* desc, int32_t partition_size) {
+  if (check_desc(desc, false) || check_partition(partition_size)) return -1;
+  return split_layout(desc, partitions(desc, partition_size)).total;
 }
 
 int kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
@@ -193,7 +212,7 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
   p.out = out;
   p.partition_blocks = desc->max_blocks_per_seq;
   p.num_partitions = 1;
-  return hip_status(pkv::launch_decode(p, desc->kv_dtype, desc->head_dim, false,
+  return hip_status(pkv::launch_decode(p, desc->kv_dtype, desc->head_dim, 0,
                                        static_cast<hipStream_t>(stream)),
                     "paged_decode_attention launch");
 }
@@ -216,9 +235,42 @@ int paged_decode_attention_partial(const void* q, const void* k_cache, const voi
   p.tmp_lse = tmp_lse;
   p.partition_blocks = partition_size / 16;
   p.num_partitions = static_cast<int32_t>(s);
-  return hip_status(pkv::launch_decode(p, desc->kv_dtype, desc->head_dim, true,
+  return hip_status(pkv::launch_decode(p, desc->kv_dtype, desc->head_dim, 1,
                                        static_cast<hipStream_t>(stream)),
                     "paged_decode_attention_partial launch");
+}
+
+int paged_decode_attention_split(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 float scale, const float* kv_scales, int32_t partition_size,
+                                 void* workspace, int64_t workspace_bytes, void* out,
+                                 const pkv_desc* desc, void* stream) {
+  if (int e = check_desc(desc, true)) return e;
+  if (int e = check_attn_types(desc, kv_scales)) return e;
+  if (int e = check_partition(partition_size)) return e;
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  if (desc->num_seqs == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !workspace || !out)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(PKV_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const int64_t s = partitions(desc, partition_size);
+  if (s > 0x7FFFFFFF) return fail(PKV_ERR_INVALID_ARG, "too many partitions");
+  const SplitLayout lay = split_layout(desc, s);
+  if (workspace_bytes < lay.total)
+    return fail(PKV_ERR_INVALID_ARG, "workspace of %lld bytes is smaller than the %lld needed",
+                static_cast<long long>(workspace_bytes), static_cast<long long>(lay.total));
+  char* ws = static_cast<char*>(workspace);
+  pkv::DecodeParams p = decode_params(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales, desc);
+  p.out = out;
+  p.counters = reinterpret_cast<int32_t*>(ws);
+  p.tmp_lse = reinterpret_cast<float*>(ws + lay.lse_off);
+  p.tmp_out = reinterpret_cast<float*>(ws + lay.out_off);
+  p.partition_blocks = partition_size / 16;
+  p.num_partitions = static_cast<int32_t>(s);
+  return hip_status(pkv::launch_decode(p, desc->kv_dtype, desc->head_dim, 2,
+                                       static_cast<hipStream_t>(stream)),
+                    "paged_decode_attention_split launch");
 }
 
 int paged_decode_attention_reduce(const float* tmp_out, const float* tmp_lse,

@@ -31,6 +31,8 @@
 #include "pkv_common.h"
 #include "pkv_launch.h"
 
+#include <algorithm>
+
 namespace pkv {
 
 // ------------------------------------------------------------ tile traits
@@ -205,9 +207,108 @@ __device__ __forceinline__ void store4(void* base, size_t idx, int out_dtype, f3
   }
 }
 
+// ----------------------------------------------------------------- merge
+// One wave merges one (sequence, query head)'s n partitions:
+// out = sum_p w_p o_p / sum_p w_p with w_p = exp(lse_p - max lse).  Lane s
+// holds partition s's weight (64 partitions per pass); partial rows are
+// fetched eight at a time so their loads overlap.  Returns this lane's D/64
+// output dims (lane * D/64 + k).
+template <int D, bool COH>
+__device__ __forceinline__ void merge_partitions(const float* lse, const float* o_row0, int n, int lane,
+                                                 float (&acc)[D / 64]) {
+  constexpr int PER = D / 64;
+  constexpr int BATCH = 8;
+  // COH: the partials were written by other workgroups in this launch, so
+  // they are read with device-scope (sc1) loads, which do not hit stale L2
+  // lines of this XCD.
+  const auto lse_r = make_tile_rsrc(lse, n * 4);
+  const auto o_r = make_tile_rsrc(o_row0, n * D * 4);
+  auto ld_lse = [&](int s) -> float {
+    if constexpr (COH) return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lse_r, s * 4, 0, kDeviceScope));
+    else return lse[s];
+  };
+  auto ld_o = [&](int s, int k) -> float {
+    if constexpr (COH)
+      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(o_r, (s * D + lane * PER + k) * 4, 0, kDeviceScope));
+    else return o_row0[static_cast<size_t>(s) * D + lane * PER + k];
+  };
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  float M = -INFINITY;
+  for (int c = 0; c < n; c += 64) M = fmaxf(M, (c + lane < n) ? ld_lse(c + lane) : -INFINITY);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float wsum = 0.f;
+  for (int c = 0; c < n; c += 64) {
+    const float w = (c + lane < n) ? fast_exp2((ld_lse(c + lane) - M) * kLog2e) : 0.f;
+    wsum += w;
+    const int cnt = min(64, n - c);
+    for (int j = 0; j < cnt; j += BATCH) {
+      float v[BATCH][PER];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        if (j + u < cnt) {
+#pragma unroll
+          for (int k = 0; k < PER; ++k) v[u][k] = ld_o(c + j + u, k);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        if (j + u < cnt) {
+          const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u));
+#pragma unroll
+          for (int k = 0; k < PER; ++k) acc[k] += wu * v[u][k];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+  const float inv = 1.f / wsum;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] *= inv;
+}
+
+template <int D>
+__device__ __forceinline__ void store_row_part(void* out, size_t row, int lane, int out_dtype,
+                                               const float (&acc)[D / 64]) {
+  constexpr int PER = D / 64;
+  const size_t idx = row * D + lane * PER;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if (out_dtype == KV_F32) static_cast<float*>(out)[idx + k] = acc[k];
+    else if (out_dtype == KV_F16) static_cast<_Float16*>(out)[idx + k] = static_cast<_Float16>(acc[k]);
+    else static_cast<__bf16*>(out)[idx + k] = static_cast<__bf16>(acc[k]);
+  }
+}
+
 // ----------------------------------------------------------------- kernel
-template <int KVT, int D, int NW, bool PARTIAL>
-__global__ __launch_bounds__(NW * 64) void paged_decode_kernel(const DecodeParams p) {
+// MODE_FINAL: one partition covers the whole context; write out.
+// MODE_PARTIAL: write each partition's (o, lse) to the workspace.
+// MODE_SPLIT: as PARTIAL, but a sequence with a single partition writes out
+// directly, and for the others the last partition to finish (counted with a
+// device-scope atomic per (sequence, kv head)) merges them into out and
+// resets the counter to zero.
+enum { MODE_FINAL = 0, MODE_PARTIAL = 1, MODE_SPLIT = 2 };
+
+// Largest amount (log2 units) a logit may exceed the running reference max
+// before the accumulators are rescaled; keeps every p = exp2(x - m) <= 2^8.
+constexpr float kSlack = 8.0f;
+
+// Workgroup-shared state of one work item: the NW waves' softmax states for
+// the cross-wave merge, and the merge ticket of the split mode.
+template <int NW, int NT>
+struct ItemShared {
+  float m[NW][16];
+  float l[NW][16];
+  f32x4 o[NW][NT][64];
+  int ticket;
+};
+
+// One work item: sequence b, kv head h, partition `part` of the context.
+template <int KVT, int D, int NW, int MODE, int PF>
+__device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h, int part,
+                                            ItemShared<NW, D / 16>& sm) {
   typedef TileOps<KVT, D> T;
   constexpr int E = ElemBytes<KVT>::value;
   constexpr int TILE = kBlockSize * D * E;  // bytes of one (block, kv head) tile
@@ -218,27 +319,19 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(const DecodeParam
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane >> 4;   // lane group: tokens 4g..4g+3 of a block
   const int r = lane & 15;   // head column (outputs) / token or dim row (loads)
-  const int part = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
   const int G = p.group;
   const int Hq = p.num_q_heads;
 
-  const int L = max(0, min(p.context_lens[b], p.mbps * kBlockSize));
-  const int nblk = (L + kBlockSize - 1) / kBlockSize;
+  const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.mbps;
   const int blk0 = part * p.partition_blocks;
-
-  if (!PARTIAL && L == 0) {  // empty context: zero output
-    if (r < G) {
-      const size_t row = (static_cast<size_t>(b) * Hq + h * G + r) * D;
-      for (int n = wid; n < NT; n += NW) store4(p.out, row + 16 * n + 4 * g, p.out_dtype, f32x4{0.f, 0.f, 0.f, 0.f});
-    }
-    return;
-  }
-  if (blk0 >= nblk) return;
-  const int blk1 = min(nblk, blk0 + p.partition_blocks);
-
-  // Query operand of this lane's head column (zero for columns >= G).
+  // Issue the loads that do not depend on the context length (this wave's
+  // first 64 block ids, bounded by the table row, and the query operand)
+  // together with the context-length load, so the prologue costs one memory
+  // latency, not three.
+  const int first = blk0 + wid;
+  const int id0 = first + NW * lane;
+  int ids = (id0 < p.mbps) ? table[id0] : 0;
+  const int L = max(0, min(p.context_lens[b], p.mbps * kBlockSize));
   const int qhead = h * G + r;
   const char* qrow = (r < G) ? static_cast<const char*>(p.q) +
                                    (static_cast<size_t>(b) * Hq + qhead) * D * (KVT == KV_F32 ? 4 : 2)
@@ -246,21 +339,39 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(const DecodeParam
   u32x4 qop[T::NQ];
   T::load_q(qop, qrow, g);
 
-  // Blocks of this wave: blk0 + wid + NW * i, i < nmine.
-  const int first = blk0 + wid;
-  const int nmine = first < blk1 ? (blk1 - first + NW - 1) / NW : 0;
-  const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.mbps;
+  const int nblk = (L + kBlockSize - 1) / kBlockSize;
+  const int nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
 
-  const size_t blk_stride = static_cast<size_t>(p.num_kv_heads) * TILE;
-  const char* kbase = static_cast<const char*>(p.k_cache) + static_cast<size_t>(h) * TILE + lane * 16;
-  const char* vbase = static_cast<const char*>(p.v_cache) + static_cast<size_t>(h) * TILE + lane * 16;
+  if (MODE != MODE_PARTIAL && L == 0) {  // empty context: zero output
+    if (part == 0 && r < G) {
+      const size_t row = (static_cast<size_t>(b) * Hq + h * G + r) * D;
+      for (int n = wid; n < NT; n += NW) store4(p.out, row + 16 * n + 4 * g, p.out_dtype, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+    return;
+  }
+  if (blk0 >= nblk) return;
+  const int blk1 = min(nblk, blk0 + p.partition_blocks);
+  const bool direct = (MODE == MODE_FINAL) || (MODE == MODE_SPLIT && nparts == 1);
+
+  // Blocks of this wave: first + NW * i, i < nmine.
+  const int nmine = first < blk1 ? (blk1 - first + NW - 1) / NW : 0;
+
+  // Tile loads are buffer loads: each tile's descriptor (base = the tile,
+  // size = TILE bytes) lives in scalar registers and every lane adds one
+  // 32-bit offset, so no per-tile 64-bit vector addresses are needed.
+  uint32_t lane_off[NL];
+#pragma unroll
+  for (int m = 0; m < NL; ++m) lane_off[m] = static_cast<uint32_t>(lane) * 16u + m * 1024u;
+  const char* kcache = static_cast<const char*>(p.k_cache);
+  const char* vcache = static_cast<const char*>(p.v_cache);
   auto load_tile = [&](u32x4 (&kt)[NL], u32x4 (&vt)[NL], int blk) {
-    const char* kp = kbase + static_cast<size_t>(blk) * blk_stride;
-    const char* vp = vbase + static_cast<size_t>(blk) * blk_stride;
+    const size_t tile = (static_cast<size_t>(blk) * p.num_kv_heads + h) * TILE;
+    const auto kr = make_tile_rsrc(kcache + tile, TILE);
+    const auto vr = make_tile_rsrc(vcache + tile, TILE);
 #pragma unroll
-    for (int m = 0; m < NL; ++m) kt[m] = ld16(kp + m * 1024);
+    for (int m = 0; m < NL; ++m) kt[m] = buffer_ld16(kr, lane_off[m]);
 #pragma unroll
-    for (int m = 0; m < NL; ++m) vt[m] = ld16(vp + m * 1024);
+    for (int m = 0; m < NL; ++m) vt[m] = buffer_ld16(vr, lane_off[m]);
   };
 
   float m_run = -INFINITY;  // running max (base-2 logits) of head r
@@ -287,179 +398,300 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(const DecodeParam
       for (int j = 0; j < 4; ++j) x[j] = (j < nv) ? x[j] : -INFINITY;
       T::mask_v(vt, nv);
     }
+    // Lazy rescaling: the reference max m_run only moves when some head's
+    // block max exceeds it by more than kSlack (log2 units), so exp2(x - m_run)
+    // stays below 2^kSlack and the accumulators are rescaled about once per
+    // partition instead of every block.  The first block always moves it.
     const float bm = max_over_groups(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-    const float m_new = fmaxf(m_run, bm);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
+    if (__any(bm > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, bm);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[n] *= alpha;
+    }
     float pr[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - m_new);
-    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-#pragma unroll
-    for (int n = 0; n < NT; ++n) o[n] *= alpha;
+    for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - m_run);
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     T::pv(o, vt, pr, pscale);
   };
 
-  // Blocks go in chunks of up to 64: the chunk's physical ids are fetched
-  // with one vector load (lane j: the chunk's j-th block) and read out with
-  // readlane; inside a chunk the tile loads run one block ahead of the math.
-  u32x4 kA[NL], vA[NL], kB[NL], vB[NL];
+  // Blocks go in chunks of up to 64: the chunk's physical ids arrive in one
+  // vector load (lane j: the chunk's j-th block) and are read out with
+  // readlane.  Tiles stream through a ring of PF register buffers: before
+  // block j is processed, the loads of block j + PF - 1 are issued, so PF - 1
+  // tiles are in flight while the matrix cores work on one.
+  u32x4 kb[PF][NL], vb[PF][NL];
+  int bid[PF];
   for (int base = 0; base < nmine; base += 64) {
     const int cnt = min(64, nmine - base);
-    const int ids = (lane < cnt) ? table[first + NW * (base + lane)] : 0;
-    int bA = __builtin_amdgcn_readlane(ids, 0), bB = 0;
-    load_tile(kA, vA, bA);
-    int i = 0;
-    for (; i + 1 < cnt; i += 2) {
-      bB = __builtin_amdgcn_readlane(ids, i + 1);
-      load_tile(kB, vB, bB);
-      process(kA, vA, base + i, bA);
-      if (i + 2 < cnt) {
-        bA = __builtin_amdgcn_readlane(ids, i + 2);
-        load_tile(kA, vA, bA);
+    if (base > 0) ids = (lane < cnt) ? table[first + NW * (base + lane)] : 0;
+#pragma unroll
+    for (int s = 0; s < PF - 1; ++s) {
+      if (s < cnt) {
+        bid[s] = __builtin_amdgcn_readlane(ids, s);
+        load_tile(kb[s], vb[s], bid[s]);
       }
-      process(kB, vB, base + i + 1, bB);
     }
-    if (i < cnt) process(kA, vA, base + i, bA);
+    for (int i = 0; i < cnt; i += PF) {
+#pragma unroll
+      for (int s = 0; s < PF; ++s) {
+        const int j = i + s;
+        if (j < cnt) {
+          const int nxt = j + PF - 1;
+          const int slot = (s + PF - 1) % PF;
+          if (nxt < cnt) {
+            bid[slot] = __builtin_amdgcn_readlane(ids, nxt);
+            load_tile(kb[slot], vb[slot], bid[slot]);
+          }
+          process(kb[s], vb[s], base + j, bid[s]);
+        }
+      }
+    }
   }
 
   l_run = sum_over_groups(l_run);
 
   // ---- merge the NW waves' (max, sum, accumulator) and write
+  const size_t out_row = (static_cast<size_t>(b) * Hq + qhead) * D;
+  const size_t part_row = (static_cast<size_t>(b) * Hq + qhead) * p.num_partitions + part;
+  // Split mode: partials go out with device-scope (sc1) stores, complete at
+  // the device coherence point once the wave's store counter drains.
+  const auto part_r = make_tile_rsrc(p.tmp_out + part_row * D, D * 4);
+  auto emit = [&](int n, f32x4 acc) {
+    if (r < G) {
+      if (direct) store4(p.out, out_row + 16 * n + 4 * g, p.out_dtype, acc);
+      else if (MODE == MODE_SPLIT)
+        __builtin_amdgcn_raw_buffer_store_b128(bitcast<u32x4>(acc), part_r, (16 * n + 4 * g) * 4, 0, kDeviceScope);
+      else *reinterpret_cast<f32x4*>(p.tmp_out + part_row * D + 16 * n + 4 * g) = acc;
+    }
+  };
   float M, Lsum;
-  float fw[NW];
   if constexpr (NW > 1) {
-    __shared__ float sm_m[NW][16];
-    __shared__ float sm_l[NW][16];
-    __shared__ f32x4 sm_o[NW][NT][64];
     if (g == 0) {
-      sm_m[wid][r] = m_run;
-      sm_l[wid][r] = l_run;
+      sm.m[wid][r] = m_run;
+      sm.l[wid][r] = l_run;
     }
 #pragma unroll
-    for (int n = 0; n < NT; ++n) sm_o[wid][n][lane] = o[n];
+    for (int n = 0; n < NT; ++n) sm.o[wid][n][lane] = o[n];
     __syncthreads();
-    M = sm_m[0][r];
+    float fw[NW];
+    M = sm.m[0][r];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][r]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm.m[w][r]);
     Lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      fw[w] = fast_exp2(sm_m[w][r] - M);
-      Lsum += fw[w] * sm_l[w][r];
+      fw[w] = fast_exp2(sm.m[w][r] - M);
+      Lsum += fw[w] * sm.l[w][r];
     }
     const float inv = 1.f / Lsum;
     for (int n = wid; n < NT; n += NW) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < NW; ++w) acc += fw[w] * sm_o[w][n][lane];
-      acc *= inv;
-      if (r < G) {
-        if constexpr (PARTIAL) {
-          const size_t row = ((static_cast<size_t>(b) * Hq + qhead) * p.num_partitions + part) * D;
-          *reinterpret_cast<f32x4*>(p.tmp_out + row + 16 * n + 4 * g) = acc;
-        } else {
-          const size_t row = (static_cast<size_t>(b) * Hq + qhead) * D;
-          store4(p.out, row + 16 * n + 4 * g, p.out_dtype, acc);
-        }
-      }
+      for (int w = 0; w < NW; ++w) acc += fw[w] * sm.o[w][n][lane];
+      emit(n, acc * inv);
     }
   } else {
     M = m_run;
     Lsum = l_run;
     const float inv = 1.f / Lsum;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const f32x4 acc = o[n] * inv;
-      if (r < G) {
-        if constexpr (PARTIAL) {
-          const size_t row = ((static_cast<size_t>(b) * Hq + qhead) * p.num_partitions + part) * D;
-          *reinterpret_cast<f32x4*>(p.tmp_out + row + 16 * n + 4 * g) = acc;
-        } else {
-          const size_t row = (static_cast<size_t>(b) * Hq + qhead) * D;
-          store4(p.out, row + 16 * n + 4 * g, p.out_dtype, acc);
-        }
-      }
-    }
+    for (int n = 0; n < NT; ++n) emit(n, o[n] * inv);
   }
-  if constexpr (PARTIAL) {
+  if (direct) return;
+  const float lse = (M + fast_log2(Lsum)) * kLn2;
+  if constexpr (MODE == MODE_SPLIT) {
     if (wid == 0 && g == 0 && r < G)
-      p.tmp_lse[(static_cast<size_t>(b) * Hq + qhead) * p.num_partitions + part] =
-          (M + fast_log2(Lsum)) * kLn2;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), make_tile_rsrc(p.tmp_lse + part_row, 4), 0, 0,
+                                            kDeviceScope);
+    // Count this partition once all its waves' partial stores are complete
+    // at device scope; the workgroup that takes the last ticket merges.
+    // No cache maintenance is needed: the partials are written and read
+    // with device-scope accesses, and the counter is a device atomic.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    int* counter = p.counters + static_cast<size_t>(b) * p.num_kv_heads + h;
+    if (threadIdx.x == 0) sm.ticket = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (sm.ticket != nparts - 1) return;
+    for (int gg = wid; gg < G; gg += NW) {
+      const size_t row = static_cast<size_t>(b) * Hq + h * G + gg;
+      float acc[D / 64];
+      merge_partitions<D, true>(p.tmp_lse + row * p.num_partitions,
+                                p.tmp_out + row * p.num_partitions * D, nparts, lane, acc);
+      store_row_part<D>(p.out, row, lane, p.out_dtype, acc);
+    }
+    if (threadIdx.x == 0) *counter = 0;   // ready for the next call
+  } else {
+    if (wid == 0 && g == 0 && r < G) p.tmp_lse[part_row] = lse;
+  }
+}
+
+// One workgroup per work item (sequence, kv head, partition), partition
+// fastest: the partitions of one sequence are dispatched together, and
+// sequences in order, so sequences sharing prefix blocks read them close in
+// time.  Items past a sequence's context exit at once.
+template <int KVT, int D, int NW, int MODE, int PF>
+__global__ __launch_bounds__(NW * 64) void paged_decode_kernel(const DecodeParams p) {
+  __shared__ ItemShared<NW, D / 16> sm;
+  const int item = static_cast<int>(blockIdx.x);
+  const int part = item % p.num_partitions;
+  const int h = (item / p.num_partitions) % p.num_kv_heads;
+  const int b = item / (p.num_partitions * p.num_kv_heads);
+  decode_item<KVT, D, NW, MODE, PF>(p, b, h, part, sm);
+}
+
+// Persistent form: as many workgroups as fit on the GPU at once.  Each one
+// first counts the non-empty work items of every sequence (an exclusive
+// prefix sum in LDS), then walks item n = blockIdx.x, + gridDim.x, ... in
+// sequence-major order, mapping n back to (sequence, kv head, partition) by
+// binary search.  No workgroup is launched for an empty partition.
+constexpr int kMaxSeqsPersistent = 2048;
+
+template <int KVT, int D, int NW, int MODE, int PF>
+__global__ __launch_bounds__(NW * 64) void paged_decode_persistent(const DecodeParams p) {
+  __shared__ ItemShared<NW, D / 16> sm;
+  __shared__ int s_cum[kMaxSeqsPersistent + 1];   // items before sequence b
+  __shared__ int s_np[kMaxSeqsPersistent];        // partitions of sequence b
+  __shared__ int s_wsum[NW];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int B = p.num_seqs;
+  const int Hkv = p.num_kv_heads;
+
+  int carry = 0;
+  for (int c0 = 0; c0 < B; c0 += NW * 64) {
+    const int i = c0 + static_cast<int>(threadIdx.x);
+    int items = 0;
+    if (i < B) {
+      const int L = max(0, min(p.context_lens[i], p.mbps * kBlockSize));
+      const int nb = (L + kBlockSize - 1) / kBlockSize;
+      int np = (nb + p.partition_blocks - 1) / p.partition_blocks;
+      if (MODE != MODE_PARTIAL) np = max(np, 1);   // an empty context still writes zeros
+      s_np[i] = np;
+      items = np * Hkv;
+    }
+    // inclusive scan within the wave, then across the NW waves
+    int x = items;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wsum[wid] = x;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wid; ++w) before += s_wsum[w];
+    int total = 0;
+    for (int w = 0; w < NW; ++w) total += s_wsum[w];
+    if (i < B) s_cum[i + 1] = before + x;
+    if (i == 0) s_cum[0] = 0;
+    carry += total;
+    __syncthreads();
+  }
+  const int N = carry;
+  for (int n = blockIdx.x; n < N; n += gridDim.x) {
+    int lo = 0, hi = B;   // last b with s_cum[b] <= n
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_cum[mid] <= n) lo = mid;
+      else hi = mid;
+    }
+    const int b = lo;
+    const int local = n - s_cum[b];
+    const int np = s_np[b];
+    decode_item<KVT, D, NW, MODE, PF>(p, b, local / np, local % np, sm);
+    __syncthreads();   // the next item reuses the merge state
   }
 }
 
 // ----------------------------------------------------------------- reduce
-// One wave per (sequence, query head): out = sum_p w_p o_p / sum_p w_p with
-// w_p = exp(lse_p - max lse) over the sequence's non-empty partitions.
+// One wave per (sequence, query head) merges its non-empty partitions.
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const ReduceParams p) {
-  constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= p.num_seqs * p.num_q_heads) return;
   const int b = pair / p.num_q_heads;
   const int L = max(0, min(p.context_lens[b], p.mbps * kBlockSize));
   const int n = min((L + p.partition_size - 1) / p.partition_size, p.num_partitions);
-  const float* lse = p.tmp_lse + static_cast<size_t>(pair) * p.num_partitions;
-  const float* o = p.tmp_out + static_cast<size_t>(pair) * p.num_partitions * D + lane * PER;
-
-  float acc[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  float acc[D / 64];
   if (n > 0) {
-    float M = -INFINITY;
-    for (int s = lane; s < n; s += 64) M = fmaxf(M, lse[s]);
+    merge_partitions<D, false>(p.tmp_lse + static_cast<size_t>(pair) * p.num_partitions,
+                        p.tmp_out + static_cast<size_t>(pair) * p.num_partitions * D, n, lane, acc);
+  } else {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float wsum = 0.f;
-    for (int s = 0; s < n; ++s) {
-      const float w = fast_exp2((lse[s] - M) * kLog2e);
-      wsum += w;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] += w * o[static_cast<size_t>(s) * D + k];
-    }
-    const float inv = 1.f / wsum;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] *= inv;
+    for (int k = 0; k < D / 64; ++k) acc[k] = 0.f;
   }
-  const size_t idx = static_cast<size_t>(pair) * D + lane * PER;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    if (p.out_dtype == KV_F32) static_cast<float*>(p.out)[idx + k] = acc[k];
-    else if (p.out_dtype == KV_F16) static_cast<_Float16*>(p.out)[idx + k] = static_cast<_Float16>(acc[k]);
-    else static_cast<__bf16*>(p.out)[idx + k] = static_cast<__bf16>(acc[k]);
-  }
+  store_row_part<D>(p.out, pair, lane, p.out_dtype, acc);
 }
 
 // --------------------------------------------------------------- launchers
 constexpr int kWaves = 4;
+#ifndef PKV_PREFETCH
+#define PKV_PREFETCH 2
+#endif
+constexpr int kPrefetch = PKV_PREFETCH;  // tile buffers per wave
 
-template <int KVT, int D>
-static hipError_t launch_decode_t(const DecodeParams& p, bool partial, hipStream_t stream) {
-  const dim3 block(kWaves * 64);
-  if (partial) {
-    const dim3 grid(p.num_partitions, p.num_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL((paged_decode_kernel<KVT, D, kWaves, true>), grid, block, 0, stream, p);
+// Workgroups of `kernel` that fit on the current device at once (compute
+// units x resident workgroups per unit); queried once per kernel and device.
+template <typename K>
+static int resident_workgroups(K kernel, int block) {
+  static int cached[16] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 16 && cached[dev] > 0) return cached[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu <= 0) per_cu = 1;
+  const int n = cus * per_cu;
+  if (dev < 16) cached[dev] = n;
+  return n;
+}
+
+template <int KVT, int D, int MODE, int PF>
+static hipError_t launch_mode(const DecodeParams& p, hipStream_t stream) {
+  const int block = kWaves * 64;
+  const int64_t items = static_cast<int64_t>(p.num_partitions) * p.num_kv_heads * p.num_seqs;
+  if (items == 0) return hipSuccess;
+  if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  if (p.num_seqs <= kMaxSeqsPersistent) {
+    auto kernel = paged_decode_persistent<KVT, D, kWaves, MODE, PF>;
+    const int64_t grid = std::min<int64_t>(items, resident_workgroups(kernel, block));
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(block), 0, stream, p);
   } else {
-    const dim3 grid(1, p.num_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL((paged_decode_kernel<KVT, D, kWaves, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((paged_decode_kernel<KVT, D, kWaves, MODE, PF>), dim3(static_cast<unsigned>(items)),
+                       dim3(block), 0, stream, p);
   }
   return hipGetLastError();
 }
 
-template <int KVT>
-static hipError_t launch_decode_d(const DecodeParams& p, int head_dim, bool partial, hipStream_t s) {
-  return head_dim == 64 ? launch_decode_t<KVT, 64>(p, partial, s) : launch_decode_t<KVT, 128>(p, partial, s);
+template <int KVT, int D>
+static hipError_t launch_decode_t(DecodeParams p, int mode, hipStream_t stream) {
+  // Register budget: a K+V tile pair takes D*e/8 VGPRs per lane; keep the
+  // ring within what two waves per SIMD allow (f32 with D = 128: two tiles).
+  constexpr int kPf = (ElemBytes<KVT>::value * D >= 512) ? 2 : kPrefetch;
+  if (mode == MODE_FINAL) p.num_partitions = 1;
+  if (mode == MODE_PARTIAL) return launch_mode<KVT, D, MODE_PARTIAL, kPf>(p, stream);
+  if (mode == MODE_SPLIT) return launch_mode<KVT, D, MODE_SPLIT, kPf>(p, stream);
+  return launch_mode<KVT, D, MODE_FINAL, kPf>(p, stream);
 }
 
-hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool partial,
+template <int KVT>
+static hipError_t launch_decode_d(const DecodeParams& p, int head_dim, int mode, hipStream_t s) {
+  return head_dim == 64 ? launch_decode_t<KVT, 64>(p, mode, s) : launch_decode_t<KVT, 128>(p, mode, s);
+}
+
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, int mode,
                          hipStream_t stream) {
   switch (kv_dtype) {
-    case KV_F32: return launch_decode_d<KV_F32>(p, head_dim, partial, stream);
-    case KV_F16: return launch_decode_d<KV_F16>(p, head_dim, partial, stream);
-    case KV_BF16: return launch_decode_d<KV_BF16>(p, head_dim, partial, stream);
-    case KV_E4M3: return launch_decode_d<KV_E4M3>(p, head_dim, partial, stream);
+    case KV_F32: return launch_decode_d<KV_F32>(p, head_dim, mode, stream);
+    case KV_F16: return launch_decode_d<KV_F16>(p, head_dim, mode, stream);
+    case KV_BF16: return launch_decode_d<KV_BF16>(p, head_dim, mode, stream);
+    case KV_E4M3: return launch_decode_d<KV_E4M3>(p, head_dim, mode, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -42,6 +42,21 @@ __device__ __forceinline__ To bitcast(const From& x) {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Raw buffer access: a 128-bit descriptor (base, byte size, gfx9 dword3 with
+// a 32-bit data format) in scalar registers; reads past `bytes` return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_tile_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Cache-policy operand of buffer loads/stores selecting device (agent)
+// scope on gfx950: the access is coherent across the XCDs' L2 caches.
+constexpr int kDeviceScope = 16;
+// s_waitcnt immediate for vmcnt(0) with the other counters left alone.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -25,6 +25,7 @@ struct DecodeParams {
   int32_t partition_blocks;    // blocks per partition (final mode: covers MBPS)
   int32_t num_partitions;      // S
   int32_t out_dtype;
+  int32_t* counters;           // [B][Hkv] split mode: partitions finished (zero between calls)
 };
 
 struct ReduceParams {
@@ -57,7 +58,9 @@ struct QuantParams {
 };
 
 // Each returns hipSuccess or the launch error.
-hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool partial,
+// mode: 0 one pass to out, 1 partials to the workspace, 2 partials merged
+// in-kernel by the last partition of each (sequence, kv head).
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, int mode,
                          hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_kv_write(const WriteParams& p, hipStream_t stream);

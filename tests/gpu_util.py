@@ -88,6 +88,10 @@ def decode(w, pool, mode="split", partition_size=None, out_dtype=torch.float32, 
     if mode == "single":
         return abi.paged_decode_attention(q, k, v, tables, lens, w.scale, scales, out_dtype=out_dtype)
     P = partition_size or w.spec.partition_size
+    if mode == "fused":
+        ws = abi.split_workspace(q, k, tables, P)
+        return abi.paged_decode_attention_split(q, k, v, tables, lens, w.scale, scales, P, ws,
+                                                out_dtype=out_dtype)
     tmp_out, tmp_lse = abi.alloc_partials(q, tables.shape[1], P)
     abi.paged_decode_attention_partial(q, k, v, tables, lens, w.scale, scales, P, tmp_out, tmp_lse)
     out = torch.empty(q.shape, dtype=out_dtype, device=device)

@@ -45,8 +45,11 @@ def _announce(*what):
     print("case:", *what, flush=True)
 
 
+MODES = ["single", "split", "fused"]
+
+
 @pytest.mark.parametrize("name", NAMES)
-@pytest.mark.parametrize("mode", ["single", "split"])
+@pytest.mark.parametrize("mode", MODES)
 def test_decode_matches_oracle(name, mode):
     _announce(name, mode)
     w = workloads.generate(name, **REDUCED[name])
@@ -63,14 +66,14 @@ def test_decode_matches_oracle(name, mode):
     ("qwen25_7b_fp8", dict(num_seqs=3, head_dim=64, lengths=("uniform", 1, 500))),
     ("qwen25_1p5b", dict(num_seqs=2, lengths=("uniform", 1, 16))),             # one block or less
 ])
-@pytest.mark.parametrize("mode", ["single", "split"])
+@pytest.mark.parametrize("mode", MODES)
 def test_decode_shape_variants(name, kw, mode):
     _announce(name, kw, mode)
     w = workloads.generate(name, **kw)
     assert max_err(decode(w, gpu_pool(w), mode, partition_size=64), oracle_out(w)) <= TOL
 
 
-@pytest.mark.parametrize("mode", ["single", "split"])
+@pytest.mark.parametrize("mode", MODES)
 def test_longest_context(mode):
     """Two sequences at the 32768-token clip of the lognormal workload:
     2048 blocks each, many 64-block id chunks per wave."""
@@ -140,17 +143,58 @@ def test_partials_match_oracle_partials(P):
     assert max_err(out, ref.merge_partials(o_ref, lse_ref, w.context_lens, P)) <= TOL
 
 
-def test_partition_sizes_agree():
-    _announce("partition sweep")
+@pytest.mark.parametrize("mode", ["split", "fused"])
+def test_partition_sizes_agree(mode):
+    _announce("partition sweep", mode)
     w = workloads.generate("qwen25_1p5b", num_seqs=4, lengths=("uniform", 1, 3000))
     want = oracle_out(w)
     pool = gpu_pool(w)
     for P in (16, 64, 512, 2048, 16 * w.max_blocks_per_seq):
-        assert max_err(decode(w, pool, "split", partition_size=P), want) <= TOL, P
+        assert max_err(decode(w, pool, mode, partition_size=P), want) <= TOL, P
+
+
+@pytest.mark.parametrize("P", [16, 64, 512])
+def test_fused_split_equals_pair_bitwise_on_every_run(P):
+    """The in-kernel merge reads partials written by other workgroups of the
+    same launch; a stale or early read would change bits.  Many runs on a
+    batch with many multi-partition sequences must all equal the two-kernel
+    result exactly."""
+    _announce("fused vs pair", P)
+    from paged_kv_gqa_cache_amd import abi
+    w = workloads.generate("qwen25_7b_prefix", num_seqs=40, lengths=("uniform", 1, 4000))
+    k, v, _ = gpu_pool(w)
+    q, tables, lens = inputs(w)
+    ref_out = decode(w, (k, v, None), "split", partition_size=P)
+    ws = abi.split_workspace(q, k, tables, P)
+    outs = [abi.paged_decode_attention_split(q, k, v, tables, lens, w.scale, None, P, ws) for _ in range(25)]
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o, ref_out), f"run {i} differs"
+
+
+def test_fused_split_reuses_its_workspace():
+    """Back-to-back calls on one workspace give the same bits, and leave the
+    counter words zero; a smaller batch after a larger one works too."""
+    _announce("fused workspace reuse")
+    from paged_kv_gqa_cache_amd import abi
+    w = workloads.generate("qwen25_7b_prefix", num_seqs=24, lengths=("uniform", 1, 3000))
+    k, v, _ = gpu_pool(w)
+    q, tables, lens = inputs(w)
+    P = 256
+    ws = abi.split_workspace(q, k, tables, P)
+    outs = [abi.paged_decode_attention_split(q, k, v, tables, lens, w.scale, None, P, ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+    assert max_err(outs[0], oracle_out(w)) <= TOL
+    counters = ws[: 24 * w.spec.num_kv_heads * 4].view(torch.int32)
+    assert torch.all(counters == 0)
+    small_out = abi.paged_decode_attention_split(q[:5].contiguous(), k, v, tables[:5].contiguous(),
+                                                 lens[:5].contiguous(), w.scale, None, P, ws)
+    assert torch.equal(small_out, outs[0][:5])
 
 
 @pytest.mark.parametrize("name", ["qwen25_1p5b", "qwen25_7b_prefix", "qwen25_7b_fp8"])
-@pytest.mark.parametrize("mode", ["single", "split"])
+@pytest.mark.parametrize("mode", MODES)
 def test_out_in_query_dtype_is_fp32_out_rounded(name, mode):
     _announce("out dtype", name, mode)
     w = workloads.generate(name, **REDUCED[name])
@@ -165,7 +209,7 @@ def test_out_in_query_dtype_is_fp32_out_rounded(name, mode):
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen25_1p5b"])
-@pytest.mark.parametrize("mode", ["single", "split"])
+@pytest.mark.parametrize("mode", MODES)
 def test_context_len_one_returns_the_new_v(name, mode):
     _announce("L=1", name, mode)
     w = workloads.generate(name, num_seqs=5, lengths=("fixed", 1))
@@ -202,7 +246,7 @@ def test_equal_queries_in_a_group_are_bitwise_equal():
     assert torch.equal(o, o[:, :, :1].expand_as(o))
 
 
-@pytest.mark.parametrize("mode", ["single", "split"])
+@pytest.mark.parametrize("mode", MODES)
 def test_empty_context_gives_zeros(mode):
     _announce("empty", mode)
     w = workloads.generate("qwen25_1p5b", num_seqs=4, lengths=("uniform", 20, 200))
@@ -227,7 +271,9 @@ def test_full_size_sampled_sequences(name):
     and random others)."""
     _announce("full", name)
     w = workloads.generate(name)
-    got = decode(w, gpu_pool(w), "split").cpu().numpy()
+    pool = gpu_pool(w)
+    got = decode(w, pool, "split").cpu().numpy()
+    fused = decode(w, pool, "fused").cpu().numpy()
     L = w.context_lens
     rng = np.random.default_rng(0)
     pick = {int(np.argmax(L)), int(np.argmin(L))}
@@ -244,4 +290,6 @@ def test_full_size_sampled_sequences(name):
     sub.context_lens = w.context_lens[pick]
     want = oracle_out(sub)
     assert float(np.max(np.abs(got[pick] - want))) <= TOL
-    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(fused[pick] - want))) <= TOL
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(fused))
+    assert float(np.max(np.abs(fused - got))) <= TOL
