@@ -117,7 +117,7 @@ class Runner:
     def __init__(self, name: str, layers: int, partition_size=None, path: str = "pair"):
         import torch
         from paged_kv_gqa_cache_amd import abi, workloads
-        from tests.gpu_util import gpu_pool, inputs, to_dev
+        from paged_kv_gqa_cache_amd.pool import gpu_pool, inputs, to_dev
 
         self.torch, self.abi = torch, abi
         self.w = w = workloads.generate(name)
