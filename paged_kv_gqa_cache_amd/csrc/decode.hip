@@ -53,11 +53,10 @@ template <int KVT, int D> struct Tile16 {
   typedef uint16_t QElem;
 
   // Lane (g, r): K load m holds token r, dims [8c, 8c+8) with c = 4m + g;
-  // the q operand holds the same dims of query head r.
-  __device__ static void load_q(u32x4 (&qop)[NQ], const void* qrow, int g) {
-    const uint16_t* q = static_cast<const uint16_t*>(qrow);
+  // the q operand holds the same dims of query head r (qoff: head r's row).
+  __device__ static void load_q(u32x4 (&qop)[NQ], __amdgpu_buffer_rsrc_t qr, uint32_t qoff, int g) {
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) qop[m] = q ? ld16(q + 8 * (4 * m + g)) : u32x4{0, 0, 0, 0};
+    for (int m = 0; m < NQ; ++m) qop[m] = buffer_ld16(qr, qoff + (8 * (4 * m + g)) * 2);
   }
   __device__ static f32x4 qk(const u32x4 (&kt)[NLOAD], const u32x4 (&qop)[NQ]) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -103,10 +102,9 @@ template <int D> struct TileOps<KV_F32, D> {
   static constexpr int NLOAD = D / 16;
   static constexpr int NQ = NLOAD;
   static constexpr int NT = D / 16;
-  __device__ static void load_q(u32x4 (&qop)[NQ], const void* qrow, int g) {
-    const float* q = static_cast<const float*>(qrow);
+  __device__ static void load_q(u32x4 (&qop)[NQ], __amdgpu_buffer_rsrc_t qr, uint32_t qoff, int g) {
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) qop[m] = q ? ld16(q + 4 * (4 * m + g)) : u32x4{0, 0, 0, 0};
+    for (int m = 0; m < NQ; ++m) qop[m] = buffer_ld16(qr, qoff + (4 * (4 * m + g)) * 4);
   }
   // K load m: token r, dims [4c, 4c+4), c = 4m + g; one MFMA per dim.
   __device__ static f32x4 qk(const u32x4 (&kt)[NLOAD], const u32x4 (&qop)[NQ]) {
@@ -146,12 +144,11 @@ template <int D> struct TileOps<KV_E4M3, D> {
   static constexpr int NQ = 2 * NLOAD;
   static constexpr int NT = D / 16;
   // K load m: token r, dims [16c, 16c+16), c = 4m + g, as two halves of 8.
-  __device__ static void load_q(u32x4 (&qop)[NQ], const void* qrow, int g) {
-    const uint16_t* q = static_cast<const uint16_t*>(qrow);
+  __device__ static void load_q(u32x4 (&qop)[NQ], __amdgpu_buffer_rsrc_t qr, uint32_t qoff, int g) {
 #pragma unroll
     for (int m = 0; m < NLOAD; ++m) {
-      qop[2 * m] = q ? ld16(q + 16 * (4 * m + g)) : u32x4{0, 0, 0, 0};
-      qop[2 * m + 1] = q ? ld16(q + 16 * (4 * m + g) + 8) : u32x4{0, 0, 0, 0};
+      qop[2 * m] = buffer_ld16(qr, qoff + (16 * (4 * m + g)) * 2);
+      qop[2 * m + 1] = buffer_ld16(qr, qoff + (16 * (4 * m + g)) * 2 + 16);
     }
   }
   __device__ static f32x4 qk(const u32x4 (&kt)[NLOAD], const u32x4 (&qop)[NQ]) {
@@ -305,9 +302,41 @@ struct ItemShared {
   int ticket;
 };
 
-// One work item: sequence b, kv head h, partition `part` of the context.
+// The loads of one work item that do not depend on its math: this wave's
+// first 64 physical block ids (lane j: logical block blk0 + wid + NW*j,
+// bounded by the table row) and the query operand of the lane's head column
+// (zero for columns >= G).  Issued ahead of the item, so their latency hides
+// behind the previous item's streaming.
+template <int KVT, int D>
+struct ItemPrefetch {
+  int ids;
+  u32x4 qop[TileOps<KVT, D>::NQ];
+};
+
+template <int KVT, int D, int NW>
+__device__ __forceinline__ void item_prefetch(const DecodeParams& p, int b, int h, int part,
+                                              ItemPrefetch<KVT, D>& pf) {
+  // Buffer loads bounded by the table row / the group's q rows: lanes past
+  // the end read 0 without a branch, so no load here is conditional (a
+  // conditional load would make the compiler drain every outstanding load
+  // at the next wait).
+  constexpr int QB = (KVT == KV_F32) ? 4 : 2;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15;
+  const auto tr = make_tile_rsrc(p.block_tables + static_cast<size_t>(b) * p.mbps, p.mbps * 4);
+  const int id0 = part * p.partition_blocks + wid + NW * lane;
+  pf.ids = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(tr, static_cast<uint32_t>(id0) * 4u, 0, 0));
+  const auto qr = make_tile_rsrc(static_cast<const char*>(p.q) +
+                                     (static_cast<size_t>(b) * p.num_q_heads + h * p.group) * D * QB,
+                                 p.group * D * QB);
+  TileOps<KVT, D>::load_q(pf.qop, qr, static_cast<uint32_t>(r * D * QB), lane >> 4);
+}
+
+// One work item: sequence b (context length L), kv head h, partition `part`.
 template <int KVT, int D, int NW, int MODE, int PF>
-__device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h, int part,
+__device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h, int part, int L,
+                                            const ItemPrefetch<KVT, D>& pf,
                                             ItemShared<NW, D / 16>& sm) {
   typedef TileOps<KVT, D> T;
   constexpr int E = ElemBytes<KVT>::value;
@@ -324,21 +353,10 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
 
   const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.mbps;
   const int blk0 = part * p.partition_blocks;
-  // Issue the loads that do not depend on the context length (this wave's
-  // first 64 block ids, bounded by the table row, and the query operand)
-  // together with the context-length load, so the prologue costs one memory
-  // latency, not three.
   const int first = blk0 + wid;
-  const int id0 = first + NW * lane;
-  int ids = (id0 < p.mbps) ? table[id0] : 0;
-  const int L = max(0, min(p.context_lens[b], p.mbps * kBlockSize));
+  int ids = pf.ids;
   const int qhead = h * G + r;
-  const char* qrow = (r < G) ? static_cast<const char*>(p.q) +
-                                   (static_cast<size_t>(b) * Hq + qhead) * D * (KVT == KV_F32 ? 4 : 2)
-                             : nullptr;
-  u32x4 qop[T::NQ];
-  T::load_q(qop, qrow, g);
-
+#define qop pf.qop
   const int nblk = (L + kBlockSize - 1) / kBlockSize;
   const int nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
 
@@ -364,10 +382,13 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
   for (int m = 0; m < NL; ++m) lane_off[m] = static_cast<uint32_t>(lane) * 16u + m * 1024u;
   const char* kcache = static_cast<const char*>(p.k_cache);
   const char* vcache = static_cast<const char*>(p.v_cache);
-  auto load_tile = [&](u32x4 (&kt)[NL], u32x4 (&vt)[NL], int blk) {
+  // A load past the wave's last block still issues, through a zero-size
+  // descriptor (reads 0, no memory traffic), so the loop has no
+  // conditional loads and each wait covers exactly the tile it needs.
+  auto load_tile = [&](u32x4 (&kt)[NL], u32x4 (&vt)[NL], int blk, bool valid) {
     const size_t tile = (static_cast<size_t>(blk) * p.num_kv_heads + h) * TILE;
-    const auto kr = make_tile_rsrc(kcache + tile, TILE);
-    const auto vr = make_tile_rsrc(vcache + tile, TILE);
+    const auto kr = make_tile_rsrc(kcache + tile, valid ? TILE : 0);
+    const auto vr = make_tile_rsrc(vcache + tile, valid ? TILE : 0);
 #pragma unroll
     for (int m = 0; m < NL; ++m) kt[m] = buffer_ld16(kr, lane_off[m]);
 #pragma unroll
@@ -430,24 +451,18 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
     if (base > 0) ids = (lane < cnt) ? table[first + NW * (base + lane)] : 0;
 #pragma unroll
     for (int s = 0; s < PF - 1; ++s) {
-      if (s < cnt) {
-        bid[s] = __builtin_amdgcn_readlane(ids, s);
-        load_tile(kb[s], vb[s], bid[s]);
-      }
+      bid[s] = __builtin_amdgcn_readlane(ids, min(s, cnt - 1));
+      load_tile(kb[s], vb[s], bid[s], s < cnt);
     }
     for (int i = 0; i < cnt; i += PF) {
 #pragma unroll
       for (int s = 0; s < PF; ++s) {
         const int j = i + s;
-        if (j < cnt) {
-          const int nxt = j + PF - 1;
-          const int slot = (s + PF - 1) % PF;
-          if (nxt < cnt) {
-            bid[slot] = __builtin_amdgcn_readlane(ids, nxt);
-            load_tile(kb[slot], vb[slot], bid[slot]);
-          }
-          process(kb[s], vb[s], base + j, bid[s]);
-        }
+        const int nxt = j + PF - 1;
+        const int slot = (s + PF - 1) % PF;
+        bid[slot] = __builtin_amdgcn_readlane(ids, min(nxt, cnt - 1));
+        load_tile(kb[slot], vb[slot], bid[slot], nxt < cnt);
+        if (j < cnt) process(kb[s], vb[s], base + j, bid[s]);
       }
     }
   }
@@ -530,6 +545,8 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
   }
 }
 
+#undef qop
+
 // One workgroup per work item (sequence, kv head, partition), partition
 // fastest: the partitions of one sequence are dispatched together, and
 // sequences in order, so sequences sharing prefix blocks read them close in
@@ -541,7 +558,10 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(const DecodeParam
   const int part = item % p.num_partitions;
   const int h = (item / p.num_partitions) % p.num_kv_heads;
   const int b = item / (p.num_partitions * p.num_kv_heads);
-  decode_item<KVT, D, NW, MODE, PF>(p, b, h, part, sm);
+  ItemPrefetch<KVT, D> pf;
+  item_prefetch<KVT, D, NW>(p, b, h, part, pf);
+  const int L = max(0, min(p.context_lens[b], p.mbps * kBlockSize));
+  decode_item<KVT, D, NW, MODE, PF>(p, b, h, part, L, pf, sm);
 }
 
 // Persistent form: as many workgroups as fit on the GPU at once.  Each one
@@ -550,12 +570,14 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(const DecodeParam
 // sequence-major order, mapping n back to (sequence, kv head, partition) by
 // binary search.  No workgroup is launched for an empty partition.
 constexpr int kMaxSeqsPersistent = 2048;
+constexpr int kXcds = 8;   // accelerator complex dies of an MI355X
 
 template <int KVT, int D, int NW, int MODE, int PF>
 __global__ __launch_bounds__(NW * 64) void paged_decode_persistent(const DecodeParams p) {
   __shared__ ItemShared<NW, D / 16> sm;
   __shared__ int s_cum[kMaxSeqsPersistent + 1];   // items before sequence b
   __shared__ int s_np[kMaxSeqsPersistent];        // partitions of sequence b
+  __shared__ int s_len[kMaxSeqsPersistent];       // context length of sequence b
   __shared__ int s_wsum[NW];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -572,6 +594,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_persistent(const DecodeP
       int np = (nb + p.partition_blocks - 1) / p.partition_blocks;
       if (MODE != MODE_PARTIAL) np = max(np, 1);   // an empty context still writes zeros
       s_np[i] = np;
+      s_len[i] = L;
       items = np * Hkv;
     }
     // inclusive scan within the wave, then across the NW waves
@@ -592,19 +615,50 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_persistent(const DecodeP
     carry += total;
     __syncthreads();
   }
+  // Items are split into 8 contiguous ranges, one per XCD (workgroup w runs
+  // on XCD w % 8), and each XCD's workgroups stride through their range.
+  // Neighbouring sequences, which are the ones likely to share prefix
+  // blocks, are then read through one L2, and each XCD gets 1/8 of the
+  // items.  The grid is a multiple of 8.
   const int N = carry;
-  for (int n = blockIdx.x; n < N; n += gridDim.x) {
-    int lo = 0, hi = B;   // last b with s_cum[b] <= n
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_cum[mid] <= n) lo = mid;
-      else hi = mid;
+  const int xcd = blockIdx.x % kXcds;
+  const int per_xcd = gridDim.x / kXcds;
+  const int lo = static_cast<int>(static_cast<int64_t>(N) * xcd / kXcds);
+  const int hi = static_cast<int>(static_cast<int64_t>(N) * (xcd + 1) / kXcds);
+  // Item n -> (sequence, kv head, partition): last b with s_cum[b] <= n.
+  auto locate = [&](int n, int& b, int& h, int& part) {
+    int lo_b = 0, hi_b = B;
+    while (hi_b - lo_b > 1) {
+      const int mid = (lo_b + hi_b) >> 1;
+      if (s_cum[mid] <= n) lo_b = mid;
+      else hi_b = mid;
     }
-    const int b = lo;
+    b = lo_b;
     const int local = n - s_cum[b];
-    const int np = s_np[b];
-    decode_item<KVT, D, NW, MODE, PF>(p, b, local / np, local % np, sm);
+    h = local / s_np[b];
+    part = local % s_np[b];
+  };
+  ItemPrefetch<KVT, D> cur, nxt;
+  int b, h, part, b2, h2, part2;
+
+  int n = lo + static_cast<int>(blockIdx.x) / kXcds;
+  if (n >= hi) return;
+  locate(n, b, h, part);
+  item_prefetch<KVT, D, NW>(p, b, h, part, cur);
+  while (true) {
+    // The next item's ids and q load while this item streams (the last item
+    // prefetches itself again, so the load is never conditional).
+    const int n2 = n + per_xcd;
+    locate(min(n2, hi - 1), b2, h2, part2);
+    item_prefetch<KVT, D, NW>(p, b2, h2, part2, nxt);
+    decode_item<KVT, D, NW, MODE, PF>(p, b, h, part, s_len[b], cur, sm);
     __syncthreads();   // the next item reuses the merge state
+    if (n2 >= hi) break;
+    n = n2;
+    b = b2;
+    h = h2;
+    part = part2;
+    cur = nxt;
   }
 }
 
@@ -660,7 +714,8 @@ static hipError_t launch_mode(const DecodeParams& p, hipStream_t stream) {
   if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   if (p.num_seqs <= kMaxSeqsPersistent) {
     auto kernel = paged_decode_persistent<KVT, D, kWaves, MODE, PF>;
-    const int64_t grid = std::min<int64_t>(items, resident_workgroups(kernel, block));
+    int64_t grid = std::min<int64_t>(items, resident_workgroups(kernel, block));
+    grid = std::max<int64_t>(kXcds, grid / kXcds * kXcds);
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(block), 0, stream, p);
   } else {
     hipLaunchKernelGGL((paged_decode_kernel<KVT, D, kWaves, MODE, PF>), dim3(static_cast<unsigned>(items)),
