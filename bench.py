@@ -128,6 +128,7 @@ class Runner:
         self.q, self.tables, self.lens = inputs(w)
         self.tmp_out, self.tmp_lse = abi.alloc_partials(self.q, self.tables.shape[1], self.P)
         self.ws = abi.split_workspace(self.q, base[0], self.tables, self.P)
+        self.bws = abi.balanced_workspace(self.q, base[0], self.tables) if path == "balanced" else None
         self.path = path
         self.out = torch.empty(self.q.shape, dtype={"f32": torch.float32, "f16": torch.float16,
                                                     "bf16": torch.bfloat16}[s.q_dtype], device="cuda")
@@ -149,7 +150,12 @@ class Runner:
             abi.kv_cache_write(self.new[0], self.new[1], self.new[2], k, v)
         if ev is not None:
             ev.record(e0, stream)
-        if self.path == "fused":
+        if self.path == "balanced":
+            abi.paged_decode_attention_balanced(self.q, k, v, self.tables, self.lens, self.w.scale, sc,
+                                                self.bws, out=self.out)
+            if ev is not None:
+                ev.record(e0 + 1, stream)
+        elif self.path == "fused":
             abi.paged_decode_attention_split(self.q, k, v, self.tables, self.lens, self.w.scale, sc,
                                              self.P, self.ws, out=self.out)
             if ev is not None:
@@ -217,8 +223,11 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="layer pools rotated through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--path", choices=["pair", "fused"], default="pair",
-                    help="partial + reduce kernels, or the one-launch split with in-kernel merge")
+    ap.add_argument("--path", choices=["pair", "fused", "balanced"], default="pair",
+                    help="partial + reduce kernels, the one-launch split with in-kernel merge, or "
+                         "equal tile shares per wave + merge")
+    ap.add_argument("--secondary-path", choices=["pair", "fused", "balanced"], default="fused",
+                    help="path for the B=32 line (its fastest: the one-launch split)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 256 MiB device to device (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -248,9 +257,9 @@ def main():
 
     b32 = None
     if not args.no_secondary and args.workload != SECONDARY:
-        r2 = Runner(SECONDARY, args.layers, None, args.path)
+        r2 = Runner(SECONDARY, args.layers, None, args.secondary_path)
         t2, p2 = r2.run(args.steps, args.warmup)
-        b32 = {"workload": f"{SECONDARY}: {DESCRIPTIONS[SECONDARY]}", "path": args.path,
+        b32 = {"workload": f"{SECONDARY}: {DESCRIPTIONS[SECONDARY]}", "path": args.secondary_path,
                "partition_size": r2.P, "us_per_step": round(t2 * 1e6, 2),
                "dominant_kernel_us": round(sum(p2) / len(p2) * 1e3, 2),
                "kv_GBps": round(r2.unique_bytes / t2 / 1e9, 1),
@@ -287,8 +296,9 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": counters_traffic(args.workload, digest),
-            "kernel": ("paged_decode_persistent, split partial mode" if args.path == "pair"
-                       else "paged_decode_persistent, split mode with in-kernel merge"),
+            "kernel": {"pair": "paged_decode_persistent, split partial mode",
+                       "fused": "paged_decode_persistent, split mode with in-kernel merge",
+                       "balanced": "paged_decode_stream + stream_merge_kernel (both inside the events)"}[args.path],
         },
         "b32": b32,
         "kernel_source_digest": digest,

@@ -218,6 +218,38 @@ int paged_decode_attention_split(const void* q, const void* k_cache, const void*
 /* Workspace bytes paged_decode_attention_split needs, or -1.  */
 int64_t paged_decode_split_workspace_bytes(const pkv_desc* desc, int32_t partition_size);
 
+/*
+ * paged_decode_attention_balanced - the same attention output, with the
+ * split-context work cut so that every wave of the GPU gets an equal share
+ * of 16-token tiles whatever the mix of context lengths (flash-decoding's
+ * split and log-sum-exp merge as above, with split points chosen by load
+ * instead of at fixed partition_size boundaries).  The tiles of all
+ * (sequence, kv head) pairs form one stream, sequence-major, and each wave
+ * takes one contiguous stretch of it; where a stretch ends inside a
+ * (sequence, kv head), both pieces become partials merged by log-sum-exp in
+ * a second kernel on the same stream.  Arguments as paged_decode_attention,
+ * plus:
+ *
+ *   workspace        device memory of workspace_bytes >=
+ *                    paged_decode_balanced_workspace_bytes(desc) bytes,
+ *                    256-byte aligned, holding per-sequence tile offsets and
+ *                    the partials.  No clearing is needed; calls that run at
+ *                    the same time must not share a workspace.
+ * Requires num_seqs <= 2048 (else PKV_ERR_UNSUPPORTED) and
+ * num_seqs * num_kv_heads * max_blocks_per_seq < 2^31.  The summation order
+ * depends on the batch's total length and the GPU's compute-unit count, so
+ * results agree with the other entry points to rounding, not bitwise.
+ */
+int paged_decode_attention_balanced(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    float scale, const float* kv_scales, void* workspace,
+                                    int64_t workspace_bytes, void* out, const pkv_desc* desc,
+                                    void* stream);
+
+/* Workspace bytes paged_decode_attention_balanced needs on the current
+ * device (it grows with the number of waves the device holds), or -1.  */
+int64_t paged_decode_balanced_workspace_bytes(const pkv_desc* desc);
+
 /* S = ceil(MBPS * 16 / partition_size), or -1 on invalid arguments.  */
 int64_t paged_decode_num_partitions(const pkv_desc* desc, int32_t partition_size);
 

@@ -56,6 +56,8 @@ def _load():
         "paged_decode_attention_reduce": (ctypes.c_int, [P, P, P, I32, P, D, P]),
         "paged_decode_attention_split": (ctypes.c_int, [P, P, P, P, P, F, P, I32, P, I64, P, D, P]),
         "paged_decode_split_workspace_bytes": (ctypes.c_int64, [D, I32]),
+        "paged_decode_attention_balanced": (ctypes.c_int, [P, P, P, P, P, F, P, P, I64, P, D, P]),
+        "paged_decode_balanced_workspace_bytes": (ctypes.c_int64, [D]),
         "paged_decode_num_partitions": (ctypes.c_int64, [D, I32]),
         "paged_decode_workspace_bytes": (ctypes.c_int64, [D, I32]),
         "pkv_last_error": (ctypes.c_char_p, []),
@@ -71,6 +73,7 @@ _lib = _load()
 EXPORTED = ("kv_cache_write", "kv_cache_quantize_e4m3", "paged_decode_attention",
             "paged_decode_attention_partial", "paged_decode_attention_reduce",
             "paged_decode_attention_split", "paged_decode_split_workspace_bytes",
+            "paged_decode_attention_balanced", "paged_decode_balanced_workspace_bytes",
             "paged_decode_num_partitions", "paged_decode_workspace_bytes", "pkv_last_error",
             "pkv_version")
 
@@ -208,5 +211,27 @@ def paged_decode_attention_split(q, k_cache, v_cache, block_tables, context_lens
     _check("paged_decode_attention_split", _lib.paged_decode_attention_split(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         float(scale), _ptr(kv_scales), int(partition_size), _ptr(workspace), workspace.numel(),
+        _ptr(out), ctypes.byref(desc), _stream(stream)))
+    return out
+
+
+def balanced_workspace(q, k_cache, block_tables) -> torch.Tensor:
+    """A workspace for paged_decode_attention_balanced on q's device."""
+    desc = _attn_desc(q, k_cache, block_tables, PKV_F32)
+    with torch.cuda.device(q.device):
+        n = _lib.paged_decode_balanced_workspace_bytes(ctypes.byref(desc))
+    if n < 0:
+        raise PkvError("paged_decode_balanced_workspace_bytes", 1, last_error())
+    return torch.empty(int(n), dtype=torch.uint8, device=q.device)
+
+
+def paged_decode_attention_balanced(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales,
+                                    workspace, out=None, out_dtype=None, stream=None):
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    desc = _attn_desc(q, k_cache, block_tables, _code(out))
+    _check("paged_decode_attention_balanced", _lib.paged_decode_attention_balanced(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        float(scale), _ptr(kv_scales), _ptr(workspace), workspace.numel(),
         _ptr(out), ctypes.byref(desc), _stream(stream)))
     return out

@@ -96,6 +96,32 @@ SplitLayout split_layout(const pkv_desc* d, int64_t s) {
   return l;
 }
 
+// Balanced workspace: [seq_tiles int32 B+1 | pad to 256][tmp_lse f32 G*slots | pad]
+// [tmp_out f32 G*slots*D], slots = B*Hkv + the resident grid's wave count.
+constexpr int kMaxSeqsBalanced = 2048;
+struct BalancedLayout {
+  int64_t slots, lse_off, out_off, total;
+  int32_t workers;
+};
+int check_balanced(const pkv_desc* d) {
+  if (d->num_seqs > kMaxSeqsBalanced)
+    return fail(PKV_ERR_UNSUPPORTED, "balanced schedule takes at most %d sequences (got %d)", kMaxSeqsBalanced,
+                d->num_seqs);
+  if (static_cast<int64_t>(d->num_seqs) * d->num_kv_heads * d->max_blocks_per_seq > 0x7FFFFFFFLL)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs * num_kv_heads * max_blocks_per_seq exceeds 2^31 - 1");
+  return PKV_OK;
+}
+BalancedLayout balanced_layout(const pkv_desc* d) {
+  BalancedLayout l;
+  l.workers = pkv::stream_max_workers(d->kv_dtype, d->head_dim);
+  const int64_t G = d->num_q_heads / d->num_kv_heads;
+  l.slots = static_cast<int64_t>(d->num_seqs) * d->num_kv_heads + l.workers;
+  l.lse_off = align256((static_cast<int64_t>(d->num_seqs) + 1) * 4);
+  l.out_off = l.lse_off + align256(G * l.slots * 4);
+  l.total = l.out_off + G * l.slots * d->head_dim * 4;
+  return l;
+}
+
 int check_partition(int32_t psize) {
   if (psize <= 0 || psize % 16) return fail(PKV_ERR_INVALID_ARG, "partition_size %d is not a positive multiple of 16", psize);
   return PKV_OK;
@@ -144,6 +170,13 @@ int64_t paged_decode_workspace_bytes(const pkv_desc* desc, int32_t partition_siz
 int64_t paged_decode_split_workspace_bytes(const pkv_desc* desc, int32_t partition_size) {
   if (check_desc(desc, false) || check_partition(partition_size)) return -1;
   return split_layout(desc, partitions(desc, partition_size)).total;
+}
+
+int64_t paged_decode_balanced_workspace_bytes(const pkv_desc* desc) {
+  if (check_desc(desc, false) || check_balanced(desc)) return -1;
+  const BalancedLayout lay = balanced_layout(desc);
+  if (lay.workers <= 0) return fail(PKV_ERR_UNSUPPORTED, "kv_dtype %d", desc->kv_dtype), -1;
+  return lay.total;
 }
 
 int kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
@@ -271,6 +304,53 @@ int paged_decode_attention_split(const void* q, const void* k_cache, const void*
   return hip_status(pkv::launch_decode(p, desc->kv_dtype, desc->head_dim, 2,
                                        static_cast<hipStream_t>(stream)),
                     "paged_decode_attention_split launch");
+}
+
+int paged_decode_attention_balanced(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                    const float* kv_scales, void* workspace, int64_t workspace_bytes,
+                                    void* out, const pkv_desc* desc, void* stream) {
+  if (int e = check_desc(desc, true)) return e;
+  if (int e = check_attn_types(desc, kv_scales)) return e;
+  if (int e = check_balanced(desc)) return e;
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  if (desc->num_seqs == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !workspace || !out)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(PKV_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const BalancedLayout lay = balanced_layout(desc);
+  if (workspace_bytes < lay.total)
+    return fail(PKV_ERR_INVALID_ARG, "workspace of %lld bytes is smaller than the %lld needed",
+                static_cast<long long>(workspace_bytes), static_cast<long long>(lay.total));
+  if (lay.slots > 0x7FFFFFFF / 16) return fail(PKV_ERR_INVALID_ARG, "too many partial slots");
+  char* ws = static_cast<char*>(workspace);
+  pkv::DecodeParams p = decode_params(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales, desc);
+  p.out = out;
+  p.seq_tiles = reinterpret_cast<int32_t*>(ws);
+  p.tmp_lse = reinterpret_cast<float*>(ws + lay.lse_off);
+  p.tmp_out = reinterpret_cast<float*>(ws + lay.out_off);
+  p.num_workers = lay.workers;
+  p.num_slots = static_cast<int32_t>(lay.slots);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (int e = hip_status(pkv::launch_stream(p, desc->kv_dtype, desc->head_dim, st),
+                         "paged_decode_attention_balanced launch"))
+    return e;
+  pkv::ReduceParams r{};
+  r.tmp_out = p.tmp_out;
+  r.tmp_lse = p.tmp_lse;
+  r.context_lens = context_lens;
+  r.out = out;
+  r.num_seqs = desc->num_seqs;
+  r.num_q_heads = desc->num_q_heads;
+  r.head_dim = desc->head_dim;
+  r.mbps = desc->max_blocks_per_seq;
+  r.out_dtype = desc->out_dtype;
+  r.seq_tiles = p.seq_tiles;
+  r.num_kv_heads = desc->num_kv_heads;
+  r.num_workers = p.num_workers;
+  r.num_slots = p.num_slots;
+  return hip_status(pkv::launch_stream_merge(r, st), "paged_decode_attention_balanced merge launch");
 }
 
 int paged_decode_attention_reduce(const float* tmp_out, const float* tmp_lse,

@@ -205,62 +205,61 @@ __device__ __forceinline__ void store4(void* base, size_t idx, int out_dtype, f3
 }
 
 // ----------------------------------------------------------------- merge
-// One wave merges one (sequence, query head)'s n partitions:
-// out = sum_p w_p o_p / sum_p w_p with w_p = exp(lse_p - max lse).  Lane s
-// holds partition s's weight (64 partitions per pass); partial rows are
-// fetched eight at a time so their loads overlap.  Returns this lane's D/64
-// output dims (lane * D/64 + k).
+// One wave merges n partial rows of one (sequence, query head): row s has
+// a normalised output o_s (D floats at o_row0 + s*D) and a log-sum-exp
+// lse_s; out = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max lse).
+// The rows go in batches of eight with an online (running-max) merge, so
+// each batch's lse and o loads issue together and n <= 8 costs one round
+// trip.  Loads are bounded buffer loads (past row n they read 0 and get
+// weight 0), so none is conditional.  The order of summation is fixed:
+// s = 0, 1, ...  Returns this lane's D/64 output dims (lane * D/64 + k).
 template <int D, bool COH>
 __device__ __forceinline__ void merge_partitions(const float* lse, const float* o_row0, int n, int lane,
                                                  float (&acc)[D / 64]) {
+  // Every rounding step is spelled out (explicit FMAs, no contraction), so
+  // the in-kernel merge and the reduce kernel give the same bits.
+#pragma clang fp contract(off)
   constexpr int PER = D / 64;
   constexpr int BATCH = 8;
   // COH: the partials were written by other workgroups in this launch, so
   // they are read with device-scope (sc1) loads, which do not hit stale L2
   // lines of this XCD.
+  constexpr int aux = COH ? kDeviceScope : 0;
   const auto lse_r = make_tile_rsrc(lse, n * 4);
   const auto o_r = make_tile_rsrc(o_row0, n * D * 4);
-  auto ld_lse = [&](int s) -> float {
-    if constexpr (COH) return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lse_r, s * 4, 0, kDeviceScope));
-    else return lse[s];
-  };
-  auto ld_o = [&](int s, int k) -> float {
-    if constexpr (COH)
-      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(o_r, (s * D + lane * PER + k) * 4, 0, kDeviceScope));
-    else return o_row0[static_cast<size_t>(s) * D + lane * PER + k];
-  };
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.f;
   float M = -INFINITY;
-  for (int c = 0; c < n; c += 64) M = fmaxf(M, (c + lane < n) ? ld_lse(c + lane) : -INFINITY);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float wsum = 0.f;
-  for (int c = 0; c < n; c += 64) {
-    const float w = (c + lane < n) ? fast_exp2((ld_lse(c + lane) - M) * kLog2e) : 0.f;
-    wsum += w;
-    const int cnt = min(64, n - c);
-    for (int j = 0; j < cnt; j += BATCH) {
-      float v[BATCH][PER];
+  for (int c = 0; c < n; c += BATCH) {
+    float l[BATCH], v[BATCH][PER];
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        if (j + u < cnt) {
+    for (int u = 0; u < BATCH; ++u) {
+      l[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lse_r, (c + u) * 4, 0, aux));
 #pragma unroll
-          for (int k = 0; k < PER; ++k) v[u][k] = ld_o(c + j + u, k);
-        }
-      }
+      for (int k = 0; k < PER; ++k)
+        v[u][k] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(o_r, ((c + u) * D + lane * PER + k) * 4, 0, aux));
+    }
+    float mc = M;
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        if (j + u < cnt) {
-          const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u));
+    for (int u = 0; u < BATCH; ++u) {
+      l[u] = (c + u < n) ? l[u] * kLog2e : -INFINITY;
+      mc = fmaxf(mc, l[u]);
+    }
+    const float alpha = fast_exp2(M - mc);   // M = -inf on the first batch: alpha = 0
+    M = mc;
+    wsum *= alpha;
 #pragma unroll
-          for (int k = 0; k < PER; ++k) acc[k] += wu * v[u][k];
-        }
-      }
+    for (int k = 0; k < PER; ++k) acc[k] *= alpha;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const float w = fast_exp2(l[u] - M);
+      wsum += w;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] = __builtin_fmaf(w, v[u][k], acc[k]);
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
   const float inv = 1.f / wsum;
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] *= inv;
@@ -313,8 +312,10 @@ struct ItemPrefetch {
   u32x4 qop[TileOps<KVT, D>::NQ];
 };
 
-template <int KVT, int D, int NW>
-__device__ __forceinline__ void item_prefetch(const DecodeParams& p, int b, int h, int part,
+// Ids of blocks first + stride*j (lane j) of sequence b's table row, and
+// the q operand of kv head h's query group.
+template <int KVT, int D>
+__device__ __forceinline__ void meta_prefetch(const DecodeParams& p, int b, int h, int first, int stride,
                                               ItemPrefetch<KVT, D>& pf) {
   // Buffer loads bounded by the table row / the group's q rows: lanes past
   // the end read 0 without a branch, so no load here is conditional (a
@@ -322,10 +323,9 @@ __device__ __forceinline__ void item_prefetch(const DecodeParams& p, int b, int 
   // at the next wait).
   constexpr int QB = (KVT == KV_F32) ? 4 : 2;
   const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
   const auto tr = make_tile_rsrc(p.block_tables + static_cast<size_t>(b) * p.mbps, p.mbps * 4);
-  const int id0 = part * p.partition_blocks + wid + NW * lane;
+  const int id0 = first + stride * lane;
   pf.ids = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(tr, static_cast<uint32_t>(id0) * 4u, 0, 0));
   const auto qr = make_tile_rsrc(static_cast<const char*>(p.q) +
                                      (static_cast<size_t>(b) * p.num_q_heads + h * p.group) * D * QB,
@@ -333,46 +333,45 @@ __device__ __forceinline__ void item_prefetch(const DecodeParams& p, int b, int 
   TileOps<KVT, D>::load_q(pf.qop, qr, static_cast<uint32_t>(r * D * QB), lane >> 4);
 }
 
-// One work item: sequence b (context length L), kv head h, partition `part`.
-template <int KVT, int D, int NW, int MODE, int PF>
-__device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h, int part, int L,
-                                            const ItemPrefetch<KVT, D>& pf,
-                                            ItemShared<NW, D / 16>& sm) {
+template <int KVT, int D, int NW>
+__device__ __forceinline__ void item_prefetch(const DecodeParams& p, int b, int h, int part,
+                                              ItemPrefetch<KVT, D>& pf) {
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  meta_prefetch<KVT, D>(p, b, h, part * p.partition_blocks + wid, NW, pf);
+}
+
+// One wave's running softmax state for the G heads of a KV head: lane
+// (g, r) holds head column r's reference max, its share of the sum over
+// the tokens 4g..4g+3 of every block, and O^T d-tiles (rows 4g..4g+3).
+template <int NT>
+struct WaveState {
+  float m;
+  float l;
+  f32x4 o[NT];
+  __device__ void reset() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// Streams the blocks first + stride*i (i < count) of sequence b (context
+// length L, kv head h) through one wave's softmax state.  `ids` holds the
+// physical ids of the first 64 of them (lane j: block first + stride*j).
+template <int KVT, int D, int PF>
+__device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int h, int L, int first,
+                                              int stride, int count, int ids,
+                                              const u32x4 (&qop)[TileOps<KVT, D>::NQ],
+                                              WaveState<D / 16>& st) {
   typedef TileOps<KVT, D> T;
   constexpr int E = ElemBytes<KVT>::value;
   constexpr int TILE = kBlockSize * D * E;  // bytes of one (block, kv head) tile
   constexpr int NL = T::NLOAD;
   constexpr int NT = T::NT;
-
   const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane >> 4;   // lane group: tokens 4g..4g+3 of a block
-  const int r = lane & 15;   // head column (outputs) / token or dim row (loads)
-  const int G = p.group;
-  const int Hq = p.num_q_heads;
-
   const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.mbps;
-  const int blk0 = part * p.partition_blocks;
-  const int first = blk0 + wid;
-  int ids = pf.ids;
-  const int qhead = h * G + r;
-#define qop pf.qop
-  const int nblk = (L + kBlockSize - 1) / kBlockSize;
-  const int nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
-
-  if (MODE != MODE_PARTIAL && L == 0) {  // empty context: zero output
-    if (part == 0 && r < G) {
-      const size_t row = (static_cast<size_t>(b) * Hq + h * G + r) * D;
-      for (int n = wid; n < NT; n += NW) store4(p.out, row + 16 * n + 4 * g, p.out_dtype, f32x4{0.f, 0.f, 0.f, 0.f});
-    }
-    return;
-  }
-  if (blk0 >= nblk) return;
-  const int blk1 = min(nblk, blk0 + p.partition_blocks);
-  const bool direct = (MODE == MODE_FINAL) || (MODE == MODE_SPLIT && nparts == 1);
-
-  // Blocks of this wave: first + NW * i, i < nmine.
-  const int nmine = first < blk1 ? (blk1 - first + NW - 1) / NW : 0;
 
   // Tile loads are buffer loads: each tile's descriptor (base = the tile,
   // size = TILE bytes) lives in scalar registers and every lane adds one
@@ -382,7 +381,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
   for (int m = 0; m < NL; ++m) lane_off[m] = static_cast<uint32_t>(lane) * 16u + m * 1024u;
   const char* kcache = static_cast<const char*>(p.k_cache);
   const char* vcache = static_cast<const char*>(p.v_cache);
-  // A load past the wave's last block still issues, through a zero-size
+  // A load past the last block still issues, through a zero-size
   // descriptor (reads 0, no memory traffic), so the loop has no
   // conditional loads and each wait covers exactly the tile it needs.
   auto load_tile = [&](u32x4 (&kt)[NL], u32x4 (&vt)[NL], int blk, bool valid) {
@@ -395,14 +394,8 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
     for (int m = 0; m < NL; ++m) vt[m] = buffer_ld16(vr, lane_off[m]);
   };
 
-  float m_run = -INFINITY;  // running max (base-2 logits) of head r
-  float l_run = 0.f;        // this lane's share of the running sum
-  f32x4 o[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   auto process = [&](const u32x4 (&kt)[NL], u32x4 (&vt)[NL], int i, int blk) {
-    const int tok0 = (first + NW * i) * kBlockSize;
+    const int tok0 = (first + stride * i) * kBlockSize;
     const f32x4 s = T::qk(kt, qop);
     float f = p.qk_scale_log2;
     float pscale = 1.f;
@@ -419,24 +412,24 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
       for (int j = 0; j < 4; ++j) x[j] = (j < nv) ? x[j] : -INFINITY;
       T::mask_v(vt, nv);
     }
-    // Lazy rescaling: the reference max m_run only moves when some head's
-    // block max exceeds it by more than kSlack (log2 units), so exp2(x - m_run)
-    // stays below 2^kSlack and the accumulators are rescaled about once per
-    // partition instead of every block.  The first block always moves it.
+    // Lazy rescaling: the reference max only moves when some head's block
+    // max exceeds it by more than kSlack (log2 units), so exp2(x - m) stays
+    // below 2^kSlack and the accumulators are rescaled about once per run
+    // of blocks instead of every block.  The first block always moves it.
     const float bm = max_over_groups(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-    if (__any(bm > m_run + kSlack)) {
-      const float m_new = fmaxf(m_run, bm);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+    if (__any(bm > st.m + kSlack)) {
+      const float m_new = fmaxf(st.m, bm);
+      const float alpha = fast_exp2(st.m - m_new);
+      st.m = m_new;
+      st.l *= alpha;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) o[n] *= alpha;
+      for (int n = 0; n < NT; ++n) st.o[n] *= alpha;
     }
     float pr[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - m_run);
-    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    T::pv(o, vt, pr, pscale);
+    for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - st.m);
+    st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    T::pv(st.o, vt, pr, pscale);
   };
 
   // Blocks go in chunks of up to 64: the chunk's physical ids arrive in one
@@ -446,9 +439,9 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
   // tiles are in flight while the matrix cores work on one.
   u32x4 kb[PF][NL], vb[PF][NL];
   int bid[PF];
-  for (int base = 0; base < nmine; base += 64) {
-    const int cnt = min(64, nmine - base);
-    if (base > 0) ids = (lane < cnt) ? table[first + NW * (base + lane)] : 0;
+  for (int base = 0; base < count; base += 64) {
+    const int cnt = min(64, count - base);
+    if (base > 0) ids = (lane < cnt) ? table[first + stride * (base + lane)] : 0;
 #pragma unroll
     for (int s = 0; s < PF - 1; ++s) {
       bid[s] = __builtin_amdgcn_readlane(ids, min(s, cnt - 1));
@@ -466,7 +459,45 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
       }
     }
   }
+}
 
+// One work item: sequence b (context length L), kv head h, partition `part`.
+template <int KVT, int D, int NW, int MODE, int PF>
+__device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h, int part, int L,
+                                            const ItemPrefetch<KVT, D>& pf,
+                                            ItemShared<NW, D / 16>& sm) {
+  constexpr int NT = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  const int G = p.group;
+  const int Hq = p.num_q_heads;
+  const int blk0 = part * p.partition_blocks;
+  const int first = blk0 + wid;
+  const int qhead = h * G + r;
+  const int nblk = (L + kBlockSize - 1) / kBlockSize;
+  const int nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
+
+  if (MODE != MODE_PARTIAL && L == 0) {  // empty context: zero output
+    if (part == 0 && r < G) {
+      const size_t row = (static_cast<size_t>(b) * Hq + h * G + r) * D;
+      for (int n = wid; n < NT; n += NW) store4(p.out, row + 16 * n + 4 * g, p.out_dtype, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+    return;
+  }
+  if (blk0 >= nblk) return;
+  const int blk1 = min(nblk, blk0 + p.partition_blocks);
+  const bool direct = (MODE == MODE_FINAL) || (MODE == MODE_SPLIT && nparts == 1);
+
+  // Blocks of this wave: first + NW * i, i < nmine.
+  const int nmine = first < blk1 ? (blk1 - first + NW - 1) / NW : 0;
+  WaveState<NT> st;
+  st.reset();
+  attend_blocks<KVT, D, PF>(p, b, h, L, first, NW, nmine, pf.ids, pf.qop, st);
+  float m_run = st.m;
+  float l_run = st.l;
+  f32x4 (&o)[NT] = st.o;
   l_run = sum_over_groups(l_run);
 
   // ---- merge the NW waves' (max, sum, accumulator) and write
@@ -544,8 +575,6 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
     if (wid == 0 && g == 0 && r < G) p.tmp_lse[part_row] = lse;
   }
 }
-
-#undef qop
 
 // One workgroup per work item (sequence, kv head, partition), partition
 // fastest: the partitions of one sequence are dispatched together, and
@@ -662,6 +691,182 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_persistent(const DecodeP
   }
 }
 
+// ------------------------------------------------------ balanced schedule
+// Every wave of a resident grid is a worker with an equal share of the
+// batch's 16-token tiles, whatever the mix of context lengths.  The tiles
+// of all (sequence, kv head) items form one stream -- sequence-major, then
+// kv head, then block -- and worker w of R takes tiles [T*w/R, T*(w+1)/R).
+// A share may begin or end inside an item: each piece of an item that a
+// worker covers is a segment with its own normalised partial output and
+// log-sum-exp (flash-decoding's split, at tile granularity), and the merge
+// kernel combines an item's segments.  A segment that is a whole item
+// writes the output directly.
+//
+// Segment (item i, worker w) keeps its partial in slot i + w: along the
+// stream both i and w are non-decreasing and one of them grows at every new
+// segment, so slots never collide, and item i's segments are the slots
+// i + w0 .. i + w1 (w0, w1 the workers of its first and last tile).
+constexpr int kMinTilesPerWorker = 8;
+
+__device__ __forceinline__ int stream_workers(int T, int max_workers) {
+  return min(max_workers, (T + kMinTilesPerWorker - 1) / kMinTilesPerWorker);
+}
+// Worker holding tile t: the largest w with floor(T*w/R) <= t.
+__device__ __forceinline__ int stream_worker_of(int64_t t, int T, int R) {
+  return static_cast<int>(((t + 1) * R + T - 1) / T - 1);
+}
+
+template <int KVT, int D, int NW, int PF>
+__global__ __launch_bounds__(NW * 64) void paged_decode_stream(const DecodeParams p) {
+  constexpr int NT = D / 16;
+  __shared__ int s_cum[kMaxSeqsPersistent + 1];   // tiles before sequence b
+  __shared__ int s_len[kMaxSeqsPersistent];       // context length of sequence b
+  __shared__ int s_wsum[NW];
+  const int B = p.num_seqs;
+  const int Hkv = p.num_kv_heads;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  const int G = p.group;
+
+  // Exclusive prefix sum over sequences of Hkv * blocks (LDS).
+  int carry = 0;
+  for (int c = 0; c < B; c += NW * 64) {
+    const int i = c + static_cast<int>(threadIdx.x);
+    int tiles = 0;
+    if (i < B) {
+      const int L = max(0, min(p.context_lens[i], p.mbps * kBlockSize));
+      s_len[i] = L;
+      tiles = Hkv * ((L + kBlockSize - 1) / kBlockSize);
+    }
+    int x = tiles;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wsum[wid] = x;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wid; ++w) before += s_wsum[w];
+    int total = 0;
+    for (int w = 0; w < NW; ++w) total += s_wsum[w];
+    if (i < B) s_cum[i + 1] = before + x;
+    if (i == 0) s_cum[0] = 0;
+    carry += total;
+    __syncthreads();
+  }
+  const int T = carry;
+  // The merge kernel reads the same prefix sums.
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= B; i += NW * 64) p.seq_tiles[i] = s_cum[i];
+  if (T == 0) return;
+
+  // Workers fill 8 contiguous ranges, one per XCD (workgroup k runs on XCD
+  // k % 8), so neighbouring sequences -- the ones likely to share prefix
+  // blocks -- go through one L2; inside a range, workers spread over the
+  // workgroups first.  From here on the waves are independent.
+  const int R = stream_workers(T, p.num_workers);
+  const int xcd = blockIdx.x % kXcds;
+  const int wg_per_xcd = gridDim.x / kXcds;
+  const int r_lo = R * xcd / kXcds;
+  const int r_hi = R * (xcd + 1) / kXcds;
+  const int w = r_lo + wid * wg_per_xcd + static_cast<int>(blockIdx.x) / kXcds;
+  if (w >= r_hi) return;
+  const int t_begin = static_cast<int>(static_cast<int64_t>(T) * w / R);
+  const int t_end = static_cast<int>(static_cast<int64_t>(T) * (w + 1) / R);
+
+  // Tile t -> (sequence, kv head, block): last b with s_cum[b] <= t.
+  auto locate = [&](int t, int& b, int& h, int& j) {
+    int lo_b = 0, hi_b = B;
+    while (hi_b - lo_b > 1) {
+      const int mid = (lo_b + hi_b) >> 1;
+      if (s_cum[mid] <= t) lo_b = mid;
+      else hi_b = mid;
+    }
+    b = lo_b;
+    const int nb = (s_len[b] + kBlockSize - 1) / kBlockSize;
+    const int local = t - s_cum[b];
+    h = local / nb;
+    j = local % nb;
+  };
+
+  int t = t_begin;
+  int b, h, j0, b2, h2, j2;
+  locate(t, b, h, j0);
+  ItemPrefetch<KVT, D> cur, nxt;
+  meta_prefetch<KVT, D>(p, b, h, j0, 1, cur);
+  WaveState<NT> st;
+  while (true) {
+    const int L = s_len[b];
+    const int nb = (L + kBlockSize - 1) / kBlockSize;
+    const int j1 = min(nb, j0 + (t_end - t));
+    const int t2 = t + (j1 - j0);
+    // The next segment's ids and q load while this one streams (the last
+    // segment prefetches its own last tile again: never a conditional load).
+    locate(min(t2, t_end - 1), b2, h2, j2);
+    meta_prefetch<KVT, D>(p, b2, h2, j2, 1, nxt);
+    st.reset();
+    attend_blocks<KVT, D, PF>(p, b, h, L, j0, 1, j1 - j0, cur.ids, cur.qop, st);
+    const float l_sum = sum_over_groups(st.l);
+    const float inv = 1.f / l_sum;
+    if (r < G) {
+      if (j0 == 0 && j1 == nb) {   // the whole item: final output
+        const size_t row = (static_cast<size_t>(b) * p.num_q_heads + h * G + r) * D;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) store4(p.out, row + 16 * n + 4 * g, p.out_dtype, st.o[n] * inv);
+      } else {
+        const size_t slot = static_cast<size_t>(r) * p.num_slots + b * Hkv + h + w;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          *reinterpret_cast<f32x4*>(p.tmp_out + slot * D + 16 * n + 4 * g) = st.o[n] * inv;
+        if (g == 0) p.tmp_lse[slot] = (st.m + fast_log2(l_sum)) * kLn2;
+      }
+    }
+    if (t2 >= t_end) break;
+    t = t2;
+    b = b2;
+    h = h2;
+    j0 = j2;
+    cur = nxt;
+  }
+}
+
+// One wave per (sequence, query head): merges the item's segments when its
+// tiles were split between workers, writes zeros for an empty context.
+template <int D>
+__global__ __launch_bounds__(256) void stream_merge_kernel(const ReduceParams p) {
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= p.num_seqs * p.num_q_heads) return;
+  const int b = pair / p.num_q_heads;
+  const int qh = pair % p.num_q_heads;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int h = qh / G;
+  const int gg = qh % G;
+  // Sequence b's blocks follow from the tile offsets the stream kernel
+  // left: (seq_tiles[b + 1] - seq_tiles[b]) / Hkv.
+  const int s0 = p.seq_tiles[b];
+  const int nb = (p.seq_tiles[b + 1] - s0) / p.num_kv_heads;
+  const int T = p.seq_tiles[p.num_seqs];
+  float acc[D / 64];
+  if (nb == 0) {
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) acc[k] = 0.f;
+    store_row_part<D>(p.out, pair, lane, p.out_dtype, acc);
+    return;
+  }
+  const int R = stream_workers(T, p.num_workers);
+  const int64_t s = s0 + static_cast<int64_t>(h) * nb;
+  const int w0 = stream_worker_of(s, T, R);
+  const int w1 = stream_worker_of(s + nb - 1, T, R);
+  if (w0 == w1) return;   // one segment: its worker wrote the output
+  const size_t slot0 = static_cast<size_t>(gg) * p.num_slots + b * p.num_kv_heads + h + w0;
+  merge_partitions<D, false>(p.tmp_lse + slot0, p.tmp_out + slot0 * D, w1 - w0 + 1, lane, acc);
+  store_row_part<D>(p.out, pair, lane, p.out_dtype, acc);
+}
+
 // ----------------------------------------------------------------- reduce
 // One wave per (sequence, query head) merges its non-empty partitions.
 template <int D>
@@ -735,6 +940,23 @@ static hipError_t launch_decode_t(DecodeParams p, int mode, hipStream_t stream) 
   return launch_mode<KVT, D, MODE_FINAL, kPf>(p, stream);
 }
 
+// Balanced schedule: the grid of the stream kernel for the current device.
+template <int KVT, int D>
+static int stream_grid() {
+  constexpr int kPf = (ElemBytes<KVT>::value * D >= 512) ? 2 : kPrefetch;
+  const int res = resident_workgroups(paged_decode_stream<KVT, D, kWaves, kPf>, kWaves * 64);
+  return std::max(kXcds, res / kXcds * kXcds);
+}
+
+template <int KVT, int D>
+static hipError_t launch_stream_t(const DecodeParams& p, hipStream_t stream) {
+  constexpr int kPf = (ElemBytes<KVT>::value * D >= 512) ? 2 : kPrefetch;
+  const int grid = stream_grid<KVT, D>();
+  if (p.num_workers != grid * kWaves) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((paged_decode_stream<KVT, D, kWaves, kPf>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int KVT>
 static hipError_t launch_decode_d(const DecodeParams& p, int head_dim, int mode, hipStream_t s) {
   return head_dim == 64 ? launch_decode_t<KVT, 64>(p, mode, s) : launch_decode_t<KVT, 128>(p, mode, s);
@@ -749,6 +971,36 @@ hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, int 
     case KV_E4M3: return launch_decode_d<KV_E4M3>(p, head_dim, mode, stream);
   }
   return hipErrorInvalidValue;
+}
+
+int stream_max_workers(int kv_dtype, int head_dim) {
+  int grid = 0;
+  switch (kv_dtype) {
+    case KV_F32: grid = head_dim == 64 ? stream_grid<KV_F32, 64>() : stream_grid<KV_F32, 128>(); break;
+    case KV_F16: grid = head_dim == 64 ? stream_grid<KV_F16, 64>() : stream_grid<KV_F16, 128>(); break;
+    case KV_BF16: grid = head_dim == 64 ? stream_grid<KV_BF16, 64>() : stream_grid<KV_BF16, 128>(); break;
+    case KV_E4M3: grid = head_dim == 64 ? stream_grid<KV_E4M3, 64>() : stream_grid<KV_E4M3, 128>(); break;
+  }
+  return grid * kWaves;
+}
+
+hipError_t launch_stream(const DecodeParams& p, int kv_dtype, int head_dim, hipStream_t stream) {
+  switch (kv_dtype) {
+    case KV_F32: return head_dim == 64 ? launch_stream_t<KV_F32, 64>(p, stream) : launch_stream_t<KV_F32, 128>(p, stream);
+    case KV_F16: return head_dim == 64 ? launch_stream_t<KV_F16, 64>(p, stream) : launch_stream_t<KV_F16, 128>(p, stream);
+    case KV_BF16: return head_dim == 64 ? launch_stream_t<KV_BF16, 64>(p, stream) : launch_stream_t<KV_BF16, 128>(p, stream);
+    case KV_E4M3: return head_dim == 64 ? launch_stream_t<KV_E4M3, 64>(p, stream) : launch_stream_t<KV_E4M3, 128>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_stream_merge(const ReduceParams& p, hipStream_t stream) {
+  const int pairs = p.num_seqs * p.num_q_heads;
+  if (pairs == 0) return hipSuccess;
+  const dim3 grid((pairs + 3) / 4), block(256);
+  if (p.head_dim == 64) hipLaunchKernelGGL(stream_merge_kernel<64>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(stream_merge_kernel<128>, grid, block, 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream) {

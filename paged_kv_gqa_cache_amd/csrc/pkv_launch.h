@@ -26,6 +26,10 @@ struct DecodeParams {
   int32_t num_partitions;      // S
   int32_t out_dtype;
   int32_t* counters;           // [B][Hkv] split mode: partitions finished (zero between calls)
+  // Balanced schedule: tmp_out is [G][num_slots][D], tmp_lse [G][num_slots].
+  int32_t* seq_tiles;          // [B + 1] tiles before each sequence (written by the kernel)
+  int32_t num_workers;         // waves of the resident grid
+  int32_t num_slots;           // B * Hkv + num_workers
 };
 
 struct ReduceParams {
@@ -34,6 +38,9 @@ struct ReduceParams {
   const int32_t* context_lens;
   void* out;
   int32_t num_seqs, num_q_heads, head_dim, mbps, partition_size, num_partitions, out_dtype;
+  // Balanced schedule only.
+  const int32_t* seq_tiles;
+  int32_t num_kv_heads, num_workers, num_slots;
 };
 
 struct WriteParams {
@@ -63,6 +70,11 @@ struct QuantParams {
 hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, int mode,
                          hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
+// Balanced schedule: worker count of the resident grid on the current
+// device, the tile-stream kernel, and the merge of split items.
+int stream_max_workers(int kv_dtype, int head_dim);
+hipError_t launch_stream(const DecodeParams& p, int kv_dtype, int head_dim, hipStream_t stream);
+hipError_t launch_stream_merge(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_kv_write(const WriteParams& p, hipStream_t stream);
 hipError_t launch_quantize_e4m3(const QuantParams& p, hipStream_t stream);
 

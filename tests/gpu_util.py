@@ -11,7 +11,9 @@ from paged_kv_gqa_cache_amd.pool import (INT_DT, OUT_DT, POISON, TORCH_DT, empty
 
 def decode(w, pool, mode="split", partition_size=None, out_dtype=torch.float32, q=None,
            tables=None, lens=None, device="cuda"):
-    """Run one decode-attention step on the GPU; returns out (torch, on device)."""
+    """Run one decode-attention step on the GPU; returns out (torch, on device).
+    mode: single (one pass), split (partial + reduce), fused (split in one
+    launch) or balanced (equal tile shares per wave)."""
     k, v, scales = pool
     q0, t0, l0 = inputs(w, device)
     q = q0 if q is None else q
@@ -19,6 +21,11 @@ def decode(w, pool, mode="split", partition_size=None, out_dtype=torch.float32, 
     lens = l0 if lens is None else lens
     if mode == "single":
         return abi.paged_decode_attention(q, k, v, tables, lens, w.scale, scales, out_dtype=out_dtype)
+    if mode == "balanced":
+        ws = abi.balanced_workspace(q, k, tables)
+        ws.fill_(0xFF)   # NaN bit patterns: a slot read before it is written shows up
+        return abi.paged_decode_attention_balanced(q, k, v, tables, lens, w.scale, scales, ws,
+                                                   out_dtype=out_dtype)
     P = partition_size or w.spec.partition_size
     if mode == "fused":
         ws = abi.split_workspace(q, k, tables, P)

@@ -132,3 +132,20 @@ def test_partition_count_and_workspace_size():
     assert abi.lib().paged_decode_workspace_bytes(ctypes.byref(d), 512) == 128 * 28 * S * (128 + 1) * 4
     assert abi.lib().paged_decode_num_partitions(ctypes.byref(d), 40) == -1
     assert abi.num_partitions(533, 512) == S
+
+
+def balanced(d, ws=FAKE, nbytes=1 << 30, ptr=FAKE):
+    return abi.lib().paged_decode_attention_balanced(ptr, ptr, ptr, ptr, ptr, 0.125, None, ws, nbytes, ptr,
+                                                     ctypes.byref(d), None)
+
+
+def test_balanced_rejects_before_touching_the_device():
+    assert balanced(desc(num_seqs=2049)) == UNSUPPORTED
+    assert "2048" in abi.last_error()
+    assert abi.lib().paged_decode_balanced_workspace_bytes(ctypes.byref(desc(num_seqs=2049))) == -1
+    assert balanced(desc(), ptr=None) == INVALID
+    assert balanced(desc(), ws=ctypes.c_void_p(0x1010)) == INVALID     # not 256-byte aligned
+    assert "aligned" in abi.last_error()
+    assert balanced(desc(max_blocks_per_seq=1 << 20, num_seqs=2048, num_kv_heads=2)) == INVALID
+    assert balanced(desc(q_dtype=abi.PKV_BF16)) == UNSUPPORTED
+    assert balanced(desc(num_seqs=0), ptr=None) == OK

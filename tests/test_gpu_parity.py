@@ -45,7 +45,7 @@ def _announce(*what):
     print("case:", *what, flush=True)
 
 
-MODES = ["single", "split", "fused"]
+MODES = ["single", "split", "fused", "balanced"]
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -113,7 +113,7 @@ def test_fp8_attention_on_oracle_codes():
     k_o, v_o, s_o = oracle_pool(w)
     pool = (to_dev(k_o, "e4m3"), to_dev(v_o, "e4m3"), torch.from_numpy(s_o).cuda())
     want = oracle_out(w, (k_o, v_o, s_o))
-    for mode in ("single", "split"):
+    for mode in ("single", "split", "balanced"):
         assert max_err(decode(w, pool, mode), want) <= TOL
 
 
@@ -259,6 +259,51 @@ def test_empty_context_gives_zeros(mode):
     assert max_err(got, want) <= TOL
 
 
+# ------------------------------------------------------- balanced schedule ---
+
+@pytest.mark.parametrize("lengths", [("uniform", 1, 40), ("lognormal", 200, 1.5, 1, 6000)])
+def test_balanced_with_many_sequences(lengths):
+    """Up to the 2048-sequence limit: many items per worker (short contexts)
+    or items cut between several workers (long ones), every output row
+    against the oracle."""
+    _announce("balanced many", lengths)
+    w = workloads.generate("smollm2_360m", num_seqs=2048 if lengths[0] == "uniform" else 300,
+                           lengths=lengths)
+    assert max_err(decode(w, gpu_pool(w), "balanced"), oracle_out(w)) <= TOL
+
+
+def test_balanced_is_deterministic_and_reuses_its_workspace():
+    _announce("balanced reuse")
+    from paged_kv_gqa_cache_amd import abi
+    w = workloads.generate("qwen25_7b_prefix", num_seqs=40, lengths=("lognormal", 600, 1.0, 1, 5000))
+    k, v, _ = gpu_pool(w)
+    q, tables, lens = inputs(w)
+    ws = abi.balanced_workspace(q, k, tables)
+    outs = [abi.paged_decode_attention_balanced(q, k, v, tables, lens, w.scale, None, ws) for _ in range(10)]
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o, outs[0]), f"run {i} differs"
+    assert max_err(outs[0], oracle_out(w)) <= TOL
+    # a smaller batch on the same workspace
+    small = abi.paged_decode_attention_balanced(q[:7].contiguous(), k, v, tables[:7].contiguous(),
+                                                lens[:7].contiguous(), w.scale, None, ws)
+    sub = workloads.generate("qwen25_7b_prefix", num_seqs=40, lengths=("lognormal", 600, 1.0, 1, 5000))
+    sub.q, sub.block_tables, sub.context_lens = sub.q[:7], sub.block_tables[:7], sub.context_lens[:7]
+    assert max_err(small, oracle_out(sub)) <= TOL
+
+
+def test_balanced_rejects_too_many_sequences():
+    from paged_kv_gqa_cache_amd import abi
+    q = torch.zeros(2049, 4, 64, dtype=torch.float16, device="cuda")
+    k = torch.zeros(4, 1, 16 * 64, dtype=torch.float16, device="cuda")
+    tables = torch.zeros(2049, 1, dtype=torch.int32, device="cuda")
+    lens = torch.ones(2049, dtype=torch.int32, device="cuda")
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    with pytest.raises(abi.PkvError) as e:
+        abi.paged_decode_attention_balanced(q, k, k, tables, lens, 0.125, None, ws)
+    assert e.value.code == 2
+
+
 # ------------------------------------------------------- full-size configs ---
 
 FULL_SAMPLE = 6
@@ -274,6 +319,7 @@ def test_full_size_sampled_sequences(name):
     pool = gpu_pool(w)
     got = decode(w, pool, "split").cpu().numpy()
     fused = decode(w, pool, "fused").cpu().numpy()
+    bal = decode(w, pool, "balanced").cpu().numpy()
     L = w.context_lens
     rng = np.random.default_rng(0)
     pick = {int(np.argmax(L)), int(np.argmin(L))}
@@ -291,5 +337,7 @@ def test_full_size_sampled_sequences(name):
     want = oracle_out(sub)
     assert float(np.max(np.abs(got[pick] - want))) <= TOL
     assert float(np.max(np.abs(fused[pick] - want))) <= TOL
-    assert np.all(np.isfinite(got)) and np.all(np.isfinite(fused))
+    assert float(np.max(np.abs(bal[pick] - want))) <= TOL
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(fused)) and np.all(np.isfinite(bal))
     assert float(np.max(np.abs(fused - got))) <= TOL
+    assert float(np.max(np.abs(bal - got))) <= TOL
