@@ -25,8 +25,8 @@
 //    lane-local max over 4 values plus two cross-group shuffles per block.
 //  * P stays fp32-accurate: 16-bit PV uses P = hi + lo (two 16-bit parts,
 //    two MFMAs), so only V's own rounding is in the product.
-//  * E4M3 codes decode to fp16 with shifts/masks (value * 2^-8); the K scale
-//    and 2^8 fold into the block's logit factor, the V scale into P.
+//  * E4M3 codes decode to fp16 exactly with the packed hardware conversion;
+//    the block's K scale folds into its logit factor, its V scale into P.
 //  * Softmax runs in base 2 (log2 e folded into the scale).
 #include "pkv_common.h"
 #include "pkv_launch.h"
@@ -138,7 +138,7 @@ template <int D> struct TileOps<KV_F32, D> {
   }
 };
 
-// E4M3 KV with f16 queries: codes decode to f16 (value * 2^-8) for f16 MFMA.
+// E4M3 KV with f16 queries: codes decode to f16 (exact) for f16 MFMA.
 template <int D> struct TileOps<KV_E4M3, D> {
   static constexpr int NLOAD = D / 64;
   static constexpr int NQ = 2 * NLOAD;
@@ -156,7 +156,7 @@ template <int D> struct TileOps<KV_E4M3, D> {
 #pragma unroll
     for (int m = 0; m < NLOAD; ++m) {
       f16x8 lo, hi;
-      e4m3x16_to_f16x8x2_scaled(kt[m], lo, hi);
+      e4m3x16_to_f16x8x2(kt[m], lo, hi);
       s = mma_k32(lo, bitcast<f16x8>(qop[2 * m]), s);
       s = mma_k32(hi, bitcast<f16x8>(qop[2 * m + 1]), s);
     }
@@ -171,7 +171,9 @@ template <int D> struct TileOps<KV_E4M3, D> {
       vt[m].x &= mk; vt[m].y &= mk; vt[m].z &= mk; vt[m].w &= mk;
     }
   }
-  // pscale = V scale * 2^8 folds the block's V scale into P.
+  // pscale = V scale * 2^8: P * pscale stays well inside f16's range for the
+  // hi/lo split; the accumulator carries the 2^8, which kOutScale removes.
+  static constexpr float kOutScale = 1.f / 256.f;
   __device__ static void pv(f32x4 (&o)[NT], const u32x4 (&vt)[NLOAD], const float (&p)[4], float pscale) {
     f16x4 hi, lo;
 #pragma unroll
@@ -181,10 +183,13 @@ template <int D> struct TileOps<KV_E4M3, D> {
       hi[j] = h;
       lo[j] = static_cast<_Float16>(ps - static_cast<float>(h));
     }
+    f16x4 v[NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) o[n] = mma_k16(e4m3x4_to_f16x4_scaled(vt[n >> 2][n & 3]), hi, o[n]);
+    for (int n = 0; n < NT; ++n) v[n] = e4m3x4_to_f16x4(vt[n >> 2][n & 3]);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) o[n] = mma_k16(e4m3x4_to_f16x4_scaled(vt[n >> 2][n & 3]), lo, o[n]);
+    for (int n = 0; n < NT; ++n) o[n] = mma_k16(v[n], hi, o[n]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[n] = mma_k16(v[n], lo, o[n]);
   }
 };
 
@@ -384,8 +389,18 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int 
   // A load past the last block still issues, through a zero-size
   // descriptor (reads 0, no memory traffic), so the loop has no
   // conditional loads and each wait covers exactly the tile it needs.
-  auto load_tile = [&](u32x4 (&kt)[NL], u32x4 (&vt)[NL], int blk, bool valid) {
+  // E4M3: the block's K and V scales ride in the ring with its tile, loaded
+  // just before the tile's codes, so the wait for a tile covers its scales
+  // and never the tiles prefetched after it.
+  const auto scale_r = make_tile_rsrc(p.kv_scales, KVT == KV_E4M3 ? 2 * p.num_blocks * p.num_kv_heads * 4 : 0);
+  auto load_tile = [&](u32x4 (&kt)[NL], u32x4 (&vt)[NL], float& ksc, float& vsc, int blk, bool valid) {
     const size_t tile = (static_cast<size_t>(blk) * p.num_kv_heads + h) * TILE;
+    if constexpr (KVT == KV_E4M3) {
+      const uint32_t so = static_cast<uint32_t>(blk * p.num_kv_heads + h) * 4u;
+      ksc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(scale_r, so, 0, 0));
+      vsc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                          scale_r, so + static_cast<uint32_t>(p.num_blocks * p.num_kv_heads) * 4u, 0, 0));
+    }
     const auto kr = make_tile_rsrc(kcache + tile, valid ? TILE : 0);
     const auto vr = make_tile_rsrc(vcache + tile, valid ? TILE : 0);
 #pragma unroll
@@ -394,14 +409,14 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int 
     for (int m = 0; m < NL; ++m) vt[m] = buffer_ld16(vr, lane_off[m]);
   };
 
-  auto process = [&](const u32x4 (&kt)[NL], u32x4 (&vt)[NL], int i, int blk) {
+  auto process = [&](const u32x4 (&kt)[NL], u32x4 (&vt)[NL], float ksc, float vsc, int i) {
     const int tok0 = (first + stride * i) * kBlockSize;
     const f32x4 s = T::qk(kt, qop);
     float f = p.qk_scale_log2;
     float pscale = 1.f;
     if constexpr (KVT == KV_E4M3) {
-      f *= 256.f * p.kv_scales[static_cast<size_t>(blk) * p.num_kv_heads + h];
-      pscale = 256.f * p.kv_scales[(static_cast<size_t>(p.num_blocks) + blk) * p.num_kv_heads + h];
+      f *= ksc;
+      pscale = 256.f * vsc;
     }
     float x[4];
 #pragma unroll
@@ -438,26 +453,28 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int 
   // block j is processed, the loads of block j + PF - 1 are issued, so PF - 1
   // tiles are in flight while the matrix cores work on one.
   u32x4 kb[PF][NL], vb[PF][NL];
-  int bid[PF];
+  float ks[PF], vs[PF];
   for (int base = 0; base < count; base += 64) {
     const int cnt = min(64, count - base);
     if (base > 0) ids = (lane < cnt) ? table[first + stride * (base + lane)] : 0;
 #pragma unroll
-    for (int s = 0; s < PF - 1; ++s) {
-      bid[s] = __builtin_amdgcn_readlane(ids, min(s, cnt - 1));
-      load_tile(kb[s], vb[s], bid[s], s < cnt);
-    }
+    for (int s = 0; s < PF - 1; ++s)
+      load_tile(kb[s], vb[s], ks[s], vs[s], __builtin_amdgcn_readlane(ids, min(s, cnt - 1)), s < cnt);
     for (int i = 0; i < cnt; i += PF) {
 #pragma unroll
       for (int s = 0; s < PF; ++s) {
         const int j = i + s;
         const int nxt = j + PF - 1;
         const int slot = (s + PF - 1) % PF;
-        bid[slot] = __builtin_amdgcn_readlane(ids, min(nxt, cnt - 1));
-        load_tile(kb[slot], vb[slot], bid[slot], nxt < cnt);
-        if (j < cnt) process(kb[s], vb[s], base + j, bid[s]);
+        load_tile(kb[slot], vb[slot], ks[slot], vs[slot], __builtin_amdgcn_readlane(ids, min(nxt, cnt - 1)),
+                  nxt < cnt);
+        if (j < cnt) process(kb[s], vb[s], ks[s], vs[s], base + j);
       }
     }
+  }
+  if constexpr (KVT == KV_E4M3) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) st.o[n] *= T::kOutScale;
   }
 }
 
@@ -895,6 +912,15 @@ constexpr int kWaves = 4;
 #endif
 constexpr int kPrefetch = PKV_PREFETCH;  // tile buffers per wave
 
+// Ring depth (tile buffers per wave).  Two: one tile streams in while the
+// matrix cores work on the other.  Deeper rings (3-4, for the smaller e4m3
+// and D = 64 tiles too) measured no faster: with two waves per SIMD the
+// loads in flight already cover the memory latency.
+template <int KVT, int D>
+constexpr int ring_depth() {
+  return kPrefetch;
+}
+
 // Workgroups of `kernel` that fit on the current device at once (compute
 // units x resident workgroups per unit); queried once per kernel and device.
 template <typename K>
@@ -931,9 +957,7 @@ static hipError_t launch_mode(const DecodeParams& p, hipStream_t stream) {
 
 template <int KVT, int D>
 static hipError_t launch_decode_t(DecodeParams p, int mode, hipStream_t stream) {
-  // Register budget: a K+V tile pair takes D*e/8 VGPRs per lane; keep the
-  // ring within what two waves per SIMD allow (f32 with D = 128: two tiles).
-  constexpr int kPf = (ElemBytes<KVT>::value * D >= 512) ? 2 : kPrefetch;
+  constexpr int kPf = ring_depth<KVT, D>();
   if (mode == MODE_FINAL) p.num_partitions = 1;
   if (mode == MODE_PARTIAL) return launch_mode<KVT, D, MODE_PARTIAL, kPf>(p, stream);
   if (mode == MODE_SPLIT) return launch_mode<KVT, D, MODE_SPLIT, kPf>(p, stream);
@@ -943,14 +967,14 @@ static hipError_t launch_decode_t(DecodeParams p, int mode, hipStream_t stream) 
 // Balanced schedule: the grid of the stream kernel for the current device.
 template <int KVT, int D>
 static int stream_grid() {
-  constexpr int kPf = (ElemBytes<KVT>::value * D >= 512) ? 2 : kPrefetch;
+  constexpr int kPf = ring_depth<KVT, D>();
   const int res = resident_workgroups(paged_decode_stream<KVT, D, kWaves, kPf>, kWaves * 64);
   return std::max(kXcds, res / kXcds * kXcds);
 }
 
 template <int KVT, int D>
 static hipError_t launch_stream_t(const DecodeParams& p, hipStream_t stream) {
-  constexpr int kPf = (ElemBytes<KVT>::value * D >= 512) ? 2 : kPrefetch;
+  constexpr int kPf = ring_depth<KVT, D>();
   const int grid = stream_grid<KVT, D>();
   if (p.num_workers != grid * kWaves) return hipErrorInvalidValue;
   hipLaunchKernelGGL((paged_decode_stream<KVT, D, kWaves, kPf>), dim3(grid), dim3(kWaves * 64), 0, stream, p);

@@ -92,34 +92,21 @@ __device__ __forceinline__ f32x4 mma_k4(float a, float b, f32x4 c) {
 }
 
 // ------------------------------------------------------------------- E4M3
-// OCP E4M3 code -> fp16 bits whose value is the code's value times 2^-8:
-// the f16 exponent field takes the code's 4 exponent bits (bias 15 instead
-// of 7) and the mantissa its 3 bits, which maps normals and subnormals alike
-// (subnormal m*2^-9 becomes f16 subnormal m*2^-17).  Two codes per call:
-// bytes 0 and 1 of x -> halves 0 and 1 of the result.
-__device__ __forceinline__ uint32_t e4m3x2_to_f16x2_scaled(uint32_t x) {
-  return ((x & 0x80u) << 8) | ((x & 0x7Fu) << 7) | ((x & 0x8000u) << 16) | ((x & 0x7F00u) << 15);
+// OCP E4M3FN codes -> f16, exactly, with the gfx950 packed conversion
+// (one instruction per two codes; every E4M3 value is an f16 value).  The
+// conversion reads bytes 0-1 (first call) and 2-3 (second) of x, low byte
+// to the low half, so four codes come out in byte order.
+__device__ __forceinline__ f16x4 e4m3x4_to_f16x4(uint32_t x) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
+  const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true));
+  return bitcast<f16x4>(u32x2{a, b});
 }
-// Four codes (bytes of x) -> four f16 (value * 2^-8).
-__device__ __forceinline__ f16x4 e4m3x4_to_f16x4_scaled(uint32_t x) {
-  u32x2 r;
-  r.x = e4m3x2_to_f16x2_scaled(x);
-  r.y = e4m3x2_to_f16x2_scaled(x >> 16);
-  return bitcast<f16x4>(r);
-}
-// Sixteen codes -> two groups of eight f16 (value * 2^-8).
-__device__ __forceinline__ void e4m3x16_to_f16x8x2_scaled(u32x4 c, f16x8& lo, f16x8& hi) {
-  u32x4 a, b;
-  a.x = e4m3x2_to_f16x2_scaled(c.x);
-  a.y = e4m3x2_to_f16x2_scaled(c.x >> 16);
-  a.z = e4m3x2_to_f16x2_scaled(c.y);
-  a.w = e4m3x2_to_f16x2_scaled(c.y >> 16);
-  b.x = e4m3x2_to_f16x2_scaled(c.z);
-  b.y = e4m3x2_to_f16x2_scaled(c.z >> 16);
-  b.z = e4m3x2_to_f16x2_scaled(c.w);
-  b.w = e4m3x2_to_f16x2_scaled(c.w >> 16);
-  lo = bitcast<f16x8>(a);
-  hi = bitcast<f16x8>(b);
+// Sixteen codes (the bytes of c in order) -> two groups of eight f16.
+__device__ __forceinline__ void e4m3x16_to_f16x8x2(u32x4 c, f16x8& lo, f16x8& hi) {
+  const u32x2 c0 = bitcast<u32x2>(e4m3x4_to_f16x4(c.x)), c1 = bitcast<u32x2>(e4m3x4_to_f16x4(c.y));
+  const u32x2 c2 = bitcast<u32x2>(e4m3x4_to_f16x4(c.z)), c3 = bitcast<u32x2>(e4m3x4_to_f16x4(c.w));
+  lo = bitcast<f16x8>(u32x4{c0.x, c0.y, c1.x, c1.y});
+  hi = bitcast<f16x8>(u32x4{c2.x, c2.y, c3.x, c3.y});
 }
 
 // fp32 in [-448, 448] -> nearest OCP E4M3 code, ties to even.  Below the
