@@ -855,7 +855,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_stream(const DecodeParam
 template <int D>
 __global__ __launch_bounds__(256) void stream_merge_kernel(const ReduceParams p) {
   const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int pair = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));  // wave-uniform
   if (pair >= p.num_seqs * p.num_q_heads) return;
   const int b = pair / p.num_q_heads;
   const int qh = pair % p.num_q_heads;
@@ -889,7 +889,7 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const ReduceParams p)
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const ReduceParams p) {
   const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int pair = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));  // wave-uniform
   if (pair >= p.num_seqs * p.num_q_heads) return;
   const int b = pair / p.num_q_heads;
   const int L = max(0, min(p.context_lens[b], p.mbps * kBlockSize));
