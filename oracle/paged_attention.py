@@ -19,6 +19,14 @@ The computation (pages cited by title and section):
 * Online softmax ("PagedAttention V2 ... online softmax"; project 04) reaches,
   up to rounding order, the plain softmax(q K^T * scale) V of one query
   against the gathered context; that plain form is what this module computes.
+* Sliding-window decode ("rvLLM: High-performance LLM inference in Rust",
+  sections "Project Status" and "Changelog", list sliding-window attention;
+  "rvLLM: The Inference Engine That Lets TPUs Compete by Writing Less Kernel
+  Code", section "The flat-scan trick that makes TPU inference work": Gemma 4
+  runs 50 of its 60 layers with it).  The pages do not define the window;
+  the plain reading taken here: with a window of W tokens a query attends
+  only to the last W positions of its context, [max(0, L - W), L); W = 0
+  means the whole context.
 * Split-context ("flash-decoding") partials: each partition of the context
   yields its own normalised output and log-sum-exp, and a log-sum-exp
   weighted merge of the partials equals the full softmax.  The pages do not
@@ -149,9 +157,15 @@ def kv_cache_write_e4m3_blocks(k_cache, v_cache, kv_scales, k_blocks, v_blocks,
 
 # ---------------------------------------------------------------- gather ---
 
+def window_start(context_len: int, window: int) -> int:
+    """First attended position: max(0, L - W) for a window W > 0, else 0."""
+    return max(0, int(context_len) - int(window)) if window > 0 else 0
+
+
 def gather(k_cache, v_cache, kv_dtype: str, table_row, context_len: int,
-           kv_head: int, head_dim: int, kv_scales=None):
-    """Dense float64 K and V [L, D] of one sequence and one KV head.
+           kv_head: int, head_dim: int, kv_scales=None, start: int = 0):
+    """Dense float64 K and V [L - start, D] of one sequence and one KV head,
+    rows for positions start .. L-1.
 
     Token t lives in physical block table_row[t // 16] at offset t % 16
     ("rvllm - A Small LLM Inference Engine in Rust", section "How it's put
@@ -162,10 +176,10 @@ def gather(k_cache, v_cache, kv_dtype: str, table_row, context_len: int,
     kidx = k_tile_index(head_dim, kv_dtype)
     vidx = v_tile_index(head_dim, kv_dtype)
     L = int(context_len)
-    t = np.arange(L)
+    t = np.arange(int(start), L)
     blk = np.asarray(table_row, dtype=np.int64)[t // BLOCK_SIZE]   # physical block of token t
     off = t % BLOCK_SIZE                                             # its slot in that block
-    rows = t[:, None]
+    rows = np.arange(len(t))[:, None]                                # row r of the gathered tiles
     K = to_f64(k_cache[blk, kv_head][rows, kidx[off]], kv_dtype)
     V = to_f64(v_cache[blk, kv_head][rows, vidx[off]], kv_dtype)
     if kv_dtype == "e4m3":
@@ -184,8 +198,9 @@ def softmax_weights(q_vec, K, scale: float) -> np.ndarray:
 
 
 def decode_attention(q_raw, q_dtype: str, k_cache, v_cache, kv_dtype: str,
-                     block_tables, context_lens, scale: float, kv_scales=None):
-    """float64 [B, Hq, D]: softmax(q K^T * scale) V per sequence and query head.
+                     block_tables, context_lens, scale: float, kv_scales=None, window: int = 0):
+    """float64 [B, Hq, D]: softmax(q K^T * scale) V per sequence and query head,
+    over positions [window_start(L, window), L).
 
     Query head i reads KV head i // G with G = Hq / Hkv (contiguous groups).
     A sequence with context length 0 yields zeros.
@@ -199,27 +214,37 @@ def decode_attention(q_raw, q_dtype: str, k_cache, v_cache, kv_dtype: str,
         L = int(context_lens[b])
         if L == 0:
             continue
+        lo = window_start(L, window)
         for h in range(Hkv):
-            K, V = gather(k_cache, v_cache, kv_dtype, block_tables[b], L, h, D, kv_scales)
+            K, V = gather(k_cache, v_cache, kv_dtype, block_tables[b], L, h, D, kv_scales, lo)
             for g in range(G):
                 i = h * G + g
                 out[b, i] = softmax_weights(q[b, i], K, scale) @ V
     return out
 
 
-def num_partitions(context_len: int, partition_size: int) -> int:
-    return (int(context_len) + partition_size - 1) // partition_size
+def partition_origin(context_len: int, window: int) -> int:
+    """Token where partition 0 starts: the window start rounded down to a
+    16-token block (0 without a window)."""
+    return window_start(context_len, window) // BLOCK_SIZE * BLOCK_SIZE
+
+
+def num_partitions(context_len: int, partition_size: int, window: int = 0) -> int:
+    a = partition_origin(context_len, window)
+    return (int(context_len) - a + partition_size - 1) // partition_size
 
 
 def decode_partials(q_raw, q_dtype: str, k_cache, v_cache, kv_dtype: str,
                     block_tables, context_lens, scale: float, partition_size: int,
-                    num_slots: int, kv_scales=None):
+                    num_slots: int, kv_scales=None, window: int = 0):
     """Per-partition outputs and log-sum-exps.
 
-    Partition j of sequence b covers tokens [j P, min((j+1) P, L_b)).  For it:
-    o_j = softmax over those tokens of the scaled logits, times their V;
-    lse_j = log sum_t exp(s_t) over those tokens (natural log).  Partitions at
-    or past ceil(L_b / P) are empty: o = 0 and lse = -inf.
+    With a = partition_origin(L_b, window) and lo = window_start(L_b, window),
+    partition j of sequence b covers tokens [max(lo, a + j P), min(a + (j+1) P, L_b))
+    (without a window: [j P, min((j+1) P, L_b))).  For it: o_j = softmax over
+    those tokens of the scaled logits, times their V; lse_j = log sum_t exp(s_t)
+    over those tokens (natural log).  Partitions at or past
+    num_partitions(L_b, P, window) are empty: o = 0 and lse = -inf.
 
     Returns ``(o float64 [B, Hq, num_slots, D], lse float64 [B, Hq, num_slots])``.
     """
@@ -231,13 +256,16 @@ def decode_partials(q_raw, q_dtype: str, k_cache, v_cache, kv_dtype: str,
     lse = np.full((B, Hq, num_slots), -np.inf, dtype=np.float64)
     for b in range(B):
         L = int(context_lens[b])
+        w0 = window_start(L, window)
+        a = partition_origin(L, window)
         for h in range(Hkv):
-            K, V = gather(k_cache, v_cache, kv_dtype, block_tables[b], L, h, D, kv_scales)
+            K, V = gather(k_cache, v_cache, kv_dtype, block_tables[b], L, h, D, kv_scales, w0)
             for g in range(G):
                 i = h * G + g
-                s_all = scale * (K @ q[b, i])
-                for j in range(num_partitions(L, partition_size)):
-                    lo, hi = j * partition_size, min((j + 1) * partition_size, L)
+                s_all = scale * (K @ q[b, i])          # row r is position w0 + r
+                for j in range(num_partitions(L, partition_size, window)):
+                    lo = max(w0, a + j * partition_size) - w0
+                    hi = min(a + (j + 1) * partition_size, L) - w0
                     s = s_all[lo:hi]
                     m = np.max(s)
                     e = np.exp(s - m)
@@ -246,15 +274,15 @@ def decode_partials(q_raw, q_dtype: str, k_cache, v_cache, kv_dtype: str,
     return o, lse
 
 
-def merge_partials(o, lse, context_lens, partition_size: int) -> np.ndarray:
+def merge_partials(o, lse, context_lens, partition_size: int, window: int = 0) -> np.ndarray:
     """LSE-weighted merge: out = sum_j w_j o_j / sum_j w_j, w_j = exp(lse_j - max lse).
 
-    Only partitions j < ceil(L_b / P) take part; L_b = 0 yields zeros.
+    Only partitions j < num_partitions(L_b, P, window) take part; L_b = 0 yields zeros.
     """
     B, Hq, _, D = o.shape
     out = np.zeros((B, Hq, D), dtype=np.float64)
     for b in range(B):
-        n = num_partitions(context_lens[b], partition_size)
+        n = num_partitions(context_lens[b], partition_size, window)
         if n == 0:
             continue
         for i in range(Hq):

@@ -6,10 +6,13 @@ of the attention arithmetic, no cache layout and no FP8 quantisation, so the
 HIP library and the CPU oracle can both consume its output without sharing
 any of the computation.
 
-Five named workloads, shaped like the models the pages run (SmolLM2-360M in
+Six named workloads, shaped like the models the pages run (SmolLM2-360M in
 "rvllm - A Small LLM Inference Engine in Rust"; Qwen2.5-1.5B and Qwen2.5-7B in
 "rvLLM: High-performance LLM inference in Rust", sections "Benchmarks" and
-the head-to-head tables), one attention layer each:
+the head-to-head tables; a sliding-window layer of the kind Gemma 4 runs in
+most of its layers, "rvLLM: The Inference Engine That Lets TPUs Compete by
+Writing Less Kernel Code", section "The flat-scan trick"), one attention
+layer each:
 
 =================  ====  =======  ===  ======  ================================  ============
 name               B     Hq/Hkv   D    dtype   context lengths                   extra
@@ -20,6 +23,7 @@ qwen25_1p5b        32    12/2     128  f16     uniform [512, 4096]              
 qwen25_7b_prefix   128   28/4     128  bf16    lognormal(median 1024, sigma 1)   8-seq groups share
                                                clipped to [16, 32768]            32 prefix blocks
 qwen25_7b_fp8      64    28/4     128  e4m3    fixed 8192                        q f16
+gemma_sliding      64    32/16    128  bf16    uniform [1024, 32768]             window 1024
 =================  ====  =======  ===  ======  ================================  ============
 
 Recipe (one ``numpy.random.default_rng(seed)`` per workload, draws in this
@@ -30,6 +34,10 @@ new token's K then V [B, Hkv, D] where the workload writes one.  Values are
 float32 N(0, 1) rounded to nearest-even into f16/bf16.  Slots no sequence
 owns stay unwritten (the caller fills the pool with NaN first).  The pool
 holds ceil(1.25 x blocks needed) blocks unless the workload fixes it.
+With a window of W tokens only the blocks holding positions
+[max(0, L - W), L) get their own ids and values; every table entry before
+them points at one shared block that is never written (it keeps the
+caller's NaN fill), so a read outside the window shows up as NaN.
 Integer ranges include both ends.  For the FP8 workload K/V stay float32 and
 the consumer quantises them per (block, kv head).
 """
@@ -63,6 +71,7 @@ class WorkloadSpec:
     prefix_blocks: int = 0         # leading blocks shared inside a group
     new_token_write: bool = False  # the step starts with kv_cache_write of one token per sequence
     partition_size: int = 512      # default split-context partition (tokens)
+    window: int = 0                # sliding window in tokens (0: whole context)
 
     @property
     def group_size(self) -> int:
@@ -81,6 +90,8 @@ SPECS = {
                                      prefix_blocks=32, partition_size=512),
     "qwen25_7b_fp8": WorkloadSpec("qwen25_7b_fp8", 1005, 64, 28, 4, 128, "f16", "e4m3",
                                   ("fixed", 8192), partition_size=1024),
+    "gemma_sliding": WorkloadSpec("gemma_sliding", 1006, 64, 32, 16, 128, "bf16", "bf16",
+                                  ("uniform", 1024, 32768), partition_size=512, window=1024),
 }
 
 
@@ -159,6 +170,12 @@ def generate(name: str, **overrides) -> Workload:
     nblk = (L + BLOCK_SIZE - 1) // BLOCK_SIZE               # blocks each sequence reads
     ctx_len = L - 1 if spec.new_token_write else L.copy()   # tokens present before the step
 
+    # First block of each sequence's window (0 without a window).
+    W = spec.window
+    if W and spec.prefix_group:
+        raise ValueError("a workload has either a window or prefix sharing")
+    jlo = (np.maximum(L - W, 0) // BLOCK_SIZE) if W else np.zeros(B, dtype=np.int64)
+
     # Which logical blocks are physically shared (prefix groups).
     grp = spec.prefix_group
     shared_per_seq = np.zeros(B, dtype=np.int64)
@@ -172,7 +189,9 @@ def generate(name: str, **overrides) -> Workload:
     else:
         groups = [([b], 0) for b in range(B)]
 
-    needed = sum(n_sh for _, n_sh in groups) + int(np.sum(nblk - shared_per_seq))
+    outside = bool(np.any(jlo > 0))                         # one never-written block
+    needed = (sum(n_sh for _, n_sh in groups) + int(np.sum(nblk - shared_per_seq - jlo))
+              + int(outside))
     num_blocks = spec.num_blocks if spec.num_blocks is not None else int(math.ceil(1.25 * needed))
     if needed > num_blocks:
         raise ValueError(f"pool of {num_blocks} blocks cannot hold {needed}")
@@ -182,6 +201,10 @@ def generate(name: str, **overrides) -> Workload:
     tables = np.full((B, mbps), -1, dtype=np.int32)
     fill_blocks, fill_valid = [], []
     cursor = 0
+    outside_id = -1
+    if outside:
+        outside_id = int(perm[cursor])
+        cursor += 1
     for members, n_shared in groups:
         shared_ids = perm[cursor:cursor + n_shared]
         cursor += n_shared
@@ -191,7 +214,8 @@ def generate(name: str, **overrides) -> Workload:
         for b in members:
             ns = int(shared_per_seq[b])
             tables[b, :ns] = shared_ids[:ns]
-            for j in range(ns, int(nblk[b])):
+            tables[b, ns:ns + int(jlo[b])] = outside_id
+            for j in range(ns + int(jlo[b]), int(nblk[b])):
                 blk = int(perm[cursor])
                 cursor += 1
                 tables[b, j] = blk
@@ -224,7 +248,7 @@ def generate(name: str, **overrides) -> Workload:
         new_v = round_to(rng.standard_normal((B, Hkv, D), dtype=np.float32), spec.kv_dtype)
 
     scale = float(np.float32(1.0 / math.sqrt(D)))
-    meta = {"blocks_needed": needed}
+    meta = {"blocks_needed": needed, "outside_block": outside_id}
     return Workload(spec, num_blocks, scale, q, L.astype(np.int32), tables, fill_blocks,
                     fill_valid, fill_k, fill_v, ctx_dtype, new_slots, new_k, new_v, meta)
 
@@ -236,19 +260,22 @@ def kv_bytes(w: Workload, unique: bool = True) -> int:
     unique: each distinct (physical block, kv head) tile counted once, by the
     tokens read from it (the most tokens any sequence reads from that block).
     For E4M3 pools each touched (block, kv head) also costs two fp32 scales.
+    With a window only positions [max(0, L - W), L) are read.
     """
     e = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}[w.spec.kv_dtype]
     Hkv, D = w.spec.num_kv_heads, w.spec.head_dim
     per_tok = 2 * Hkv * D * e
     per_blk_extra = 2 * 4 * Hkv if w.spec.kv_dtype == "e4m3" else 0
     L = w.context_lens.astype(np.int64)
+    W = w.spec.window
+    lo = np.maximum(L - W, 0) if W else np.zeros_like(L)
     if not unique:
-        nb = (L + BLOCK_SIZE - 1) // BLOCK_SIZE
-        return int(L.sum() * per_tok + nb.sum() * per_blk_extra)
+        nb = (L + BLOCK_SIZE - 1) // BLOCK_SIZE - lo // BLOCK_SIZE
+        return int((L - lo).sum() * per_tok + nb.sum() * per_blk_extra)
     used = {}
     for b in range(len(L)):
-        for j in range((int(L[b]) + BLOCK_SIZE - 1) // BLOCK_SIZE):
-            toks = min(BLOCK_SIZE, int(L[b]) - j * BLOCK_SIZE)
+        for j in range(int(lo[b]) // BLOCK_SIZE, (int(L[b]) + BLOCK_SIZE - 1) // BLOCK_SIZE):
+            toks = min(BLOCK_SIZE, int(L[b]) - j * BLOCK_SIZE) - max(0, int(lo[b]) - j * BLOCK_SIZE)
             blk = int(w.block_tables[b, j])
             used[blk] = max(used.get(blk, 0), toks)
     return int(sum(used.values()) * per_tok + len(used) * per_blk_extra)

@@ -30,22 +30,23 @@ def oracle_pool(w):
     return k_cache, v_cache, kv_scales
 
 
-def logical_kv(w, b, h):
-    """float64 K, V [L_b, D] of sequence b / kv head h taken from the generator's
-    per-block arrays and new-token arrays (16-bit/f32 workloads only)."""
+def logical_kv(w, b, h, start=0):
+    """float64 K, V [L_b - start, D] (positions start .. L_b - 1) of sequence b /
+    kv head h taken from the generator's per-block arrays and new-token arrays
+    (16-bit/f32 workloads only)."""
     s = w.spec
     where = {int(blk): i for i, blk in enumerate(w.fill_blocks)}
     L = int(w.context_lens[b])
-    K = np.empty((L, s.head_dim))
-    V = np.empty((L, s.head_dim))
-    for t in range(L):
+    K = np.empty((L - start, s.head_dim))
+    V = np.empty((L - start, s.head_dim))
+    for t in range(start, L):
         if w.new_slots is not None and t == L - 1:
             kr, vr = w.new_k[b, h], w.new_v[b, h]
         else:
             i = where[int(w.block_tables[b, t // BS])]
             kr, vr = w.fill_k[i, t % BS, h], w.fill_v[i, t % BS, h]
-        K[t] = ref.to_f64(kr, s.kv_dtype)
-        V[t] = ref.to_f64(vr, s.kv_dtype)
+        K[t - start] = ref.to_f64(kr, s.kv_dtype)
+        V[t - start] = ref.to_f64(vr, s.kv_dtype)
     return K, V
 
 

@@ -367,3 +367,115 @@ def test_generator_new_token_slots_are_each_sequences_last_position():
     slots, _, _ = w.fill_tokens()
     assert not set(slots.tolist()) & set(w.new_slots.tolist())
     assert len(set(slots.tolist())) == len(slots)
+
+
+# --------------------------------------------------------- sliding window ---
+
+def _window(W, **kw):
+    base = dict(num_seqs=3, lengths=("uniform", 1, 120), head_dim=64, num_q_heads=8, num_kv_heads=4)
+    base.update(kw)
+    return small("gemma_sliding", window=W, **base)
+
+
+@pytest.mark.parametrize("W", [1, 16, 23, 64])
+def test_window_oracle_matches_python_triple_loop(W):
+    """The textbook loops over only the last W positions of each context."""
+    w = _window(W)
+    out = ref.decode_attention(w.q, "bf16", *oracle_pool(w)[:2], "bf16", w.block_tables, w.context_lens,
+                               w.scale, window=W)
+    s = w.spec
+    q = ref.to_f64(w.q, s.q_dtype)
+    for b in range(s.num_seqs):
+        lo = max(0, int(w.context_lens[b]) - W)
+        Ks, Vs = zip(*(logical_kv(w, b, h, lo) for h in range(s.num_kv_heads)))
+        bf = bruteforce.gqa_decode(q[b].tolist(), [K.tolist() for K in Ks], [V.tolist() for V in Vs], w.scale)
+        np.testing.assert_allclose(out[b], np.array(bf), rtol=0, atol=1e-12)
+
+
+def test_window_oracle_matches_torch_sdpa_on_the_window():
+    w = _window(100, num_seqs=6, lengths=("uniform", 1, 400), head_dim=128)
+    k, v, _ = oracle_pool(w)
+    out = ref.decode_attention(w.q, "bf16", k, v, "bf16", w.block_tables, w.context_lens, w.scale, window=100)
+    s = w.spec
+    q = torch.from_numpy(ref.to_f64(w.q, s.q_dtype))
+    for b in range(s.num_seqs):
+        lo = max(0, int(w.context_lens[b]) - 100)
+        Ks, Vs = zip(*(logical_kv(w, b, h, lo) for h in range(s.num_kv_heads)))
+        K = torch.from_numpy(np.stack(Ks)).repeat_interleave(s.group_size, dim=0)
+        V = torch.from_numpy(np.stack(Vs)).repeat_interleave(s.group_size, dim=0)
+        o = torch.nn.functional.scaled_dot_product_attention(q[b][:, None, :], K, V, scale=w.scale)[:, 0, :]
+        np.testing.assert_allclose(out[b], o.numpy(), rtol=0, atol=1e-12)
+
+
+def test_window_of_one_returns_the_last_v_and_no_outside_block_is_read():
+    w = _window(1, num_seqs=4, lengths=("uniform", 20, 90))
+    k, v, _ = oracle_pool(w)
+    out = ref.decode_attention(w.q, "bf16", k, v, "bf16", w.block_tables, w.context_lens, w.scale, window=1)
+    G = w.spec.group_size
+    for b in range(4):
+        for h in range(w.spec.num_kv_heads):
+            _, V = logical_kv(w, b, h, int(w.context_lens[b]) - 1)
+            for g in range(G):
+                assert np.array_equal(out[b, h * G + g], V[0])
+    # the shared outside block is never written: it keeps its NaN fill
+    ob = w.meta["outside_block"]
+    assert ob >= 0 and np.all(k[ob] == ref.POISON["bf16"])
+    assert np.all(np.isfinite(out))
+
+
+def test_window_equals_full_attention_on_the_table_shifted_by_whole_blocks():
+    """L - W a multiple of 16: attending to the window equals attending, without
+    a window, to a sequence whose table starts (L - W) / 16 blocks later."""
+    w = _window(36, num_seqs=3, lengths=("fixed", 100))
+    k, v, _ = oracle_pool(w)
+    out = ref.decode_attention(w.q, "bf16", k, v, "bf16", w.block_tables, w.context_lens, w.scale, window=36)
+    shifted = np.full_like(w.block_tables, -1)
+    shifted[:, :3] = w.block_tables[:, 4:7]
+    full = ref.decode_attention(w.q, "bf16", k, v, "bf16", shifted, np.full(3, 36, np.int32), w.scale)
+    assert np.array_equal(out, full)
+
+
+def test_window_wider_than_the_context_is_the_whole_context():
+    w = _window(4096, num_seqs=3, lengths=("uniform", 1, 300))
+    k, v, _ = oracle_pool(w)
+    a = ref.decode_attention(w.q, "bf16", k, v, "bf16", w.block_tables, w.context_lens, w.scale, window=4096)
+    b = ref.decode_attention(w.q, "bf16", k, v, "bf16", w.block_tables, w.context_lens, w.scale)
+    assert np.array_equal(a, b)
+    SDPA = torch.nn.functional.scaled_dot_product_attention
+    q = torch.from_numpy(ref.to_f64(w.q, "bf16"))
+    K, V = logical_kv(w, 0, 0)
+    o = SDPA(q[0][:2, None, :], torch.from_numpy(K)[None].expand(2, -1, -1), torch.from_numpy(V)[None].expand(2, -1, -1),
+             scale=w.scale)[:, 0, :]
+    np.testing.assert_allclose(a[0, :2], o.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("P", [16, 48, 512])
+def test_window_partials_merge_to_the_window_softmax(P):
+    W = 57
+    w = _window(W, num_seqs=5, lengths=("uniform", 1, 300))
+    k, v, _ = oracle_pool(w)
+    full = ref.decode_attention(w.q, "bf16", k, v, "bf16", w.block_tables, w.context_lens, w.scale, window=W)
+    S = max(ref.num_partitions(int(L), P, W) for L in w.context_lens)
+    o, lse = ref.decode_partials(w.q, "bf16", k, v, "bf16", w.block_tables, w.context_lens, w.scale, P, S,
+                                 window=W)
+    np.testing.assert_allclose(ref.merge_partials(o, lse, w.context_lens, P, W), full, rtol=0, atol=1e-12)
+    for b, L in enumerate(w.context_lens):
+        L = int(L)
+        lo = max(0, L - W)
+        a = lo // 16 * 16
+        n = ref.num_partitions(L, P, W)
+        assert n == -(-(L - a) // P)
+        assert np.all(np.isneginf(lse[b, :, n:]))
+        # partition 0's lse is the logsumexp of its own tokens' scaled logits
+        q = ref.to_f64(w.q, "bf16")
+        K, _ = logical_kv(w, b, 0, lo)
+        hi = min(a + P, L) - lo
+        assert abs(lse[b, 0, 0] - logsumexp(w.scale * (K[:hi] @ q[b, 0]))) <= 1e-12
+
+
+def test_window_generator_counts_only_window_bytes():
+    w = _window(40, num_seqs=4, lengths=("uniform", 1, 200))
+    L = w.context_lens.astype(int)
+    per_tok = 2 * w.spec.num_kv_heads * w.spec.head_dim * 2
+    assert workloads.kv_bytes(w, unique=False) == int(np.minimum(L, 40).sum()) * per_tok
+    assert workloads.kv_bytes(w, unique=True) == int(np.minimum(L, 40).sum()) * per_tok
