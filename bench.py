@@ -46,6 +46,8 @@ DESCRIPTIONS = {
     "qwen25_7b_fp8": "Qwen2.5-7B-shaped attention layer, FP8 E4M3 KV with per-(block, kv head) scales: "
                      "64 seqs, 28 Q / 4 KV heads, head_dim 128, context 8192, q fp16",
     "tiny": "4 seqs, 8 Q / 2 KV heads, head_dim 64, fp32, pool of 128 blocks",
+    "gemma_sliding": "sliding-window attention layer: 64 seqs, 32 Q / 16 KV heads, head_dim 128, bf16, "
+                     "window 1024 tokens, context uniform [1024, 32768]",
 }
 DTYPE_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16", "e4m3": "e4m3"}
 
@@ -152,21 +154,21 @@ class Runner:
             ev.record(e0, stream)
         if self.path == "balanced":
             abi.paged_decode_attention_balanced(self.q, k, v, self.tables, self.lens, self.w.scale, sc,
-                                                self.bws, out=self.out)
+                                                self.bws, out=self.out, window=self.spec.window)
             if ev is not None:
                 ev.record(e0 + 1, stream)
         elif self.path == "fused":
             abi.paged_decode_attention_split(self.q, k, v, self.tables, self.lens, self.w.scale, sc,
-                                             self.P, self.ws, out=self.out)
+                                             self.P, self.ws, out=self.out, window=self.spec.window)
             if ev is not None:
                 ev.record(e0 + 1, stream)
         else:
             abi.paged_decode_attention_partial(self.q, k, v, self.tables, self.lens, self.w.scale, sc,
-                                               self.P, self.tmp_out, self.tmp_lse)
+                                               self.P, self.tmp_out, self.tmp_lse, window=self.spec.window)
             if ev is not None:
                 ev.record(e0 + 1, stream)
             abi.paged_decode_attention_reduce(self.tmp_out, self.tmp_lse, self.lens, self.P, self.out,
-                                              self.tables.shape[1])
+                                              self.tables.shape[1], window=self.spec.window)
 
     def run(self, steps: int, warmup: int):
         """Returns (seconds per step, [dominant-kernel ms per step])."""

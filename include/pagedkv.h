@@ -79,6 +79,20 @@ enum pkv_status {
 
 enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_E4M3 = 3 };
 
+/*
+ * Sliding window.  With desc->sliding_window = W > 0 every attention entry
+ * point attends, for sequence b, only to positions [lo, L) with L =
+ * context_lens[b] and lo = max(0, L - W) (the pages list sliding-window
+ * attention: "rvLLM: High-performance LLM inference in Rust", sections
+ * "Project Status" and "Changelog"; Gemma 4 runs 50 of its 60 layers with it,
+ * "rvLLM: The Inference Engine That Lets TPUs Compete by Writing Less Kernel
+ * Code", section "The flat-scan trick that makes TPU inference work").  Table
+ * entries before block lo / 16 are never read, so a cache may have released
+ * them.  Partitions then start at a = 16 * floor(lo / 16): partition p covers
+ * positions [max(lo, a + p P), min(a + (p+1) P, L)), and there are
+ * ceil((L - a) / P) of them.
+ */
+
 /* Sizes and element types of one decode-attention problem.  */
 typedef struct pkv_desc {
   int32_t num_seqs;           /* B >= 0 (0: nothing to do)                    */
@@ -91,6 +105,10 @@ typedef struct pkv_desc {
   int32_t q_dtype;            /* pkv_dtype of q (and of k/v for the write)    */
   int32_t kv_dtype;           /* pkv_dtype of the caches                      */
   int32_t out_dtype;          /* pkv_dtype of out                             */
+  int32_t sliding_window;     /* W >= 0; 0: attend to the whole context; W > 0:
+                                 each query attends only to positions
+                                 [max(0, L - W), L) of its context (see
+                                 "Sliding window" above)                      */
 } pkv_desc;
 
 /*
@@ -144,7 +162,8 @@ int kv_cache_quantize_e4m3(const float* k_src, const float* v_src, const int32_t
  *   q             [B][Hq][D] in q_dtype
  *   k_cache, v_cache  [NB][Hkv][tile] in kv_dtype
  *   block_tables  int32 [B][MBPS]; entries past ceil(context_lens[b]/16)
- *                 are never read
+ *                 (and, with a sliding window, before the window's first
+ *                 block) are never read
  *   context_lens  int32 [B]; includes the token written this step; a
  *                 sequence with 0 gets a zero output
  *   scale         softmax scale (finite), usually 1/sqrt(D)

@@ -34,7 +34,7 @@ BLOCK_SIZE = 16
 class PkvDesc(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size", "num_blocks",
-        "max_blocks_per_seq", "q_dtype", "kv_dtype", "out_dtype")]
+        "max_blocks_per_seq", "q_dtype", "kv_dtype", "out_dtype", "sliding_window")]
 
 
 class PkvError(RuntimeError):
@@ -117,15 +117,16 @@ def _code(t: torch.Tensor) -> int:
 
 
 def make_desc(num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
-              q_dtype, kv_dtype, out_dtype) -> PkvDesc:
+              q_dtype, kv_dtype, out_dtype, sliding_window=0) -> PkvDesc:
     return PkvDesc(num_seqs, num_q_heads, num_kv_heads, head_dim, BLOCK_SIZE, num_blocks,
-                   max_blocks_per_seq, q_dtype, kv_dtype, out_dtype)
+                   max_blocks_per_seq, q_dtype, kv_dtype, out_dtype, sliding_window)
 
 
-def _attn_desc(q, k_cache, block_tables, out_dtype_code) -> PkvDesc:
+def _attn_desc(q, k_cache, block_tables, out_dtype_code, window=0) -> PkvDesc:
     B, Hq, D = q.shape
     NB, Hkv = k_cache.shape[0], k_cache.shape[1]
-    return make_desc(B, Hq, Hkv, D, NB, block_tables.shape[1], _code(q), _code(k_cache), out_dtype_code)
+    return make_desc(B, Hq, Hkv, D, NB, block_tables.shape[1], _code(q), _code(k_cache), out_dtype_code,
+                     int(window))
 
 
 # ---------------------------------------------------------------- entries ---
@@ -150,10 +151,10 @@ def kv_cache_quantize_e4m3(k_src, v_src, block_ids, valid_tokens, k_cache, v_cac
 
 
 def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,
-                           kv_scales=None, out=None, out_dtype=None, stream=None):
+                           kv_scales=None, out=None, out_dtype=None, stream=None, window=0):
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
-    desc = _attn_desc(q, k_cache, block_tables, _code(out))
+    desc = _attn_desc(q, k_cache, block_tables, _code(out), window)
     _check("paged_decode_attention", _lib.paged_decode_attention(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         float(scale), _ptr(kv_scales), _ptr(out), ctypes.byref(desc), _stream(stream)))
@@ -177,8 +178,9 @@ def alloc_partials(q, max_blocks_per_seq: int, partition_size: int):
 
 
 def paged_decode_attention_partial(q, k_cache, v_cache, block_tables, context_lens, scale,
-                                   kv_scales, partition_size, tmp_out, tmp_lse, stream=None) -> None:
-    desc = _attn_desc(q, k_cache, block_tables, PKV_F32)
+                                   kv_scales, partition_size, tmp_out, tmp_lse, stream=None,
+                                   window=0) -> None:
+    desc = _attn_desc(q, k_cache, block_tables, PKV_F32, window)
     _check("paged_decode_attention_partial", _lib.paged_decode_attention_partial(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         float(scale), _ptr(kv_scales), int(partition_size), _ptr(tmp_out), _ptr(tmp_lse),
@@ -186,9 +188,9 @@ def paged_decode_attention_partial(q, k_cache, v_cache, block_tables, context_le
 
 
 def paged_decode_attention_reduce(tmp_out, tmp_lse, context_lens, partition_size, out,
-                                  max_blocks_per_seq: int, stream=None) -> None:
+                                  max_blocks_per_seq: int, stream=None, window=0) -> None:
     B, Hq, S, D = tmp_out.shape
-    desc = make_desc(B, Hq, 1, D, 1, max_blocks_per_seq, PKV_F32, PKV_F32, _code(out))
+    desc = make_desc(B, Hq, 1, D, 1, max_blocks_per_seq, PKV_F32, PKV_F32, _code(out), int(window))
     _check("paged_decode_attention_reduce", _lib.paged_decode_attention_reduce(
         _ptr(tmp_out), _ptr(tmp_lse), _ptr(context_lens), int(partition_size), _ptr(out),
         ctypes.byref(desc), _stream(stream)))
@@ -204,10 +206,11 @@ def split_workspace(q, k_cache, block_tables, partition_size: int) -> torch.Tens
 
 
 def paged_decode_attention_split(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales,
-                                 partition_size, workspace, out=None, out_dtype=None, stream=None):
+                                 partition_size, workspace, out=None, out_dtype=None, stream=None,
+                                 window=0):
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
-    desc = _attn_desc(q, k_cache, block_tables, _code(out))
+    desc = _attn_desc(q, k_cache, block_tables, _code(out), window)
     _check("paged_decode_attention_split", _lib.paged_decode_attention_split(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         float(scale), _ptr(kv_scales), int(partition_size), _ptr(workspace), workspace.numel(),
@@ -226,10 +229,10 @@ def balanced_workspace(q, k_cache, block_tables) -> torch.Tensor:
 
 
 def paged_decode_attention_balanced(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales,
-                                    workspace, out=None, out_dtype=None, stream=None):
+                                    workspace, out=None, out_dtype=None, stream=None, window=0):
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
-    desc = _attn_desc(q, k_cache, block_tables, _code(out))
+    desc = _attn_desc(q, k_cache, block_tables, _code(out), window)
     _check("paged_decode_attention_balanced", _lib.paged_decode_attention_balanced(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         float(scale), _ptr(kv_scales), _ptr(workspace), workspace.numel(),

@@ -60,6 +60,7 @@ int check_desc(const pkv_desc* d, bool need_seqs) {
   if (d->max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq < 1");
   if (static_cast<int64_t>(d->max_blocks_per_seq) * 16 > (int64_t(1) << 30))
     return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq too large");
+  if (d->sliding_window < 0) return fail(PKV_ERR_INVALID_ARG, "sliding_window < 0");
   return PKV_OK;
 }
 
@@ -144,6 +145,7 @@ pkv::DecodeParams decode_params(const void* q, const void* kc, const void* vc, c
   p.num_blocks = d->num_blocks;
   p.mbps = d->max_blocks_per_seq;
   p.out_dtype = d->out_dtype;
+  p.window = d->sliding_window;
   return p;
 }
 
@@ -350,6 +352,7 @@ int paged_decode_attention_balanced(const void* q, const void* k_cache, const vo
   r.num_kv_heads = desc->num_kv_heads;
   r.num_workers = p.num_workers;
   r.num_slots = p.num_slots;
+  r.window = p.window;
   return hip_status(pkv::launch_stream_merge(r, st), "paged_decode_attention_balanced merge launch");
 }
 
@@ -377,6 +380,7 @@ int paged_decode_attention_reduce(const float* tmp_out, const float* tmp_lse,
   p.partition_size = partition_size;
   p.num_partitions = static_cast<int32_t>(partitions(desc, partition_size));
   p.out_dtype = o;
+  p.window = desc->sliding_window;
   return hip_status(pkv::launch_reduce(p, static_cast<hipStream_t>(stream)),
                     "paged_decode_attention_reduce launch");
 }

@@ -296,6 +296,12 @@ enum { MODE_FINAL = 0, MODE_PARTIAL = 1, MODE_SPLIT = 2 };
 // before the accumulators are rescaled; keeps every p = exp2(x - m) <= 2^8.
 constexpr float kSlack = 8.0f;
 
+// Sliding window: the first attended position of a context of L tokens
+// (max(0, L - W) for a window W > 0, else 0) and the block holding it, where
+// the sequence's partitions (or its run of tiles) begin.
+__device__ __forceinline__ int window_lo(int L, int window) { return window > 0 ? max(0, L - window) : 0; }
+__device__ __forceinline__ int window_block(int L, int window) { return window_lo(L, window) / kBlockSize; }
+
 // Workgroup-shared state of one work item: the NW waves' softmax states for
 // the cross-wave merge, and the merge ticket of the split mode.
 template <int NW, int NT>
@@ -339,10 +345,10 @@ __device__ __forceinline__ void meta_prefetch(const DecodeParams& p, int b, int 
 }
 
 template <int KVT, int D, int NW>
-__device__ __forceinline__ void item_prefetch(const DecodeParams& p, int b, int h, int part,
+__device__ __forceinline__ void item_prefetch(const DecodeParams& p, int b, int h, int part, int L,
                                               ItemPrefetch<KVT, D>& pf) {
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  meta_prefetch<KVT, D>(p, b, h, part * p.partition_blocks + wid, NW, pf);
+  meta_prefetch<KVT, D>(p, b, h, window_block(L, p.window) + part * p.partition_blocks + wid, NW, pf);
 }
 
 // One wave's running softmax state for the G heads of a KV head: lane
@@ -362,10 +368,11 @@ struct WaveState {
 };
 
 // Streams the blocks first + stride*i (i < count) of sequence b (context
-// length L, kv head h) through one wave's softmax state.  `ids` holds the
+// length L, kv head h, positions before lo masked off) through one wave's
+// softmax state.  `ids` holds the
 // physical ids of the first 64 of them (lane j: block first + stride*j).
 template <int KVT, int D, int PF>
-__device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int h, int L, int first,
+__device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int h, int L, int lo, int first,
                                               int stride, int count, int ids,
                                               const u32x4 (&qop)[TileOps<KVT, D>::NQ],
                                               WaveState<D / 16>& st) {
@@ -426,6 +433,11 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int 
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[j] = (j < nv) ? x[j] : -INFINITY;
       T::mask_v(vt, nv);
+    }
+    if (tok0 < lo) {              // the window's first block: positions before lo
+      const int nlo = lo - tok0 - 4 * g;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = (j < nlo) ? -INFINITY : x[j];
     }
     // Lazy rescaling: the reference max only moves when some head's block
     // max exceeds it by more than kSlack (log2 units), so exp2(x - m) stays
@@ -490,11 +502,13 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
   const int r = lane & 15;
   const int G = p.group;
   const int Hq = p.num_q_heads;
-  const int blk0 = part * p.partition_blocks;
+  const int lo = window_lo(L, p.window);
+  const int base_blk = lo / kBlockSize;     // partition 0 starts at the window's first block
+  const int blk0 = base_blk + part * p.partition_blocks;
   const int first = blk0 + wid;
   const int qhead = h * G + r;
   const int nblk = (L + kBlockSize - 1) / kBlockSize;
-  const int nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  const int nparts = (nblk - base_blk + p.partition_blocks - 1) / p.partition_blocks;
 
   if (MODE != MODE_PARTIAL && L == 0) {  // empty context: zero output
     if (part == 0 && r < G) {
@@ -511,7 +525,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
   const int nmine = first < blk1 ? (blk1 - first + NW - 1) / NW : 0;
   WaveState<NT> st;
   st.reset();
-  attend_blocks<KVT, D, PF>(p, b, h, L, first, NW, nmine, pf.ids, pf.qop, st);
+  attend_blocks<KVT, D, PF>(p, b, h, L, lo, first, NW, nmine, pf.ids, pf.qop, st);
   float m_run = st.m;
   float l_run = st.l;
   f32x4 (&o)[NT] = st.o;
@@ -604,9 +618,9 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(const DecodeParam
   const int part = item % p.num_partitions;
   const int h = (item / p.num_partitions) % p.num_kv_heads;
   const int b = item / (p.num_partitions * p.num_kv_heads);
-  ItemPrefetch<KVT, D> pf;
-  item_prefetch<KVT, D, NW>(p, b, h, part, pf);
   const int L = max(0, min(p.context_lens[b], p.mbps * kBlockSize));
+  ItemPrefetch<KVT, D> pf;
+  item_prefetch<KVT, D, NW>(p, b, h, part, L, pf);
   decode_item<KVT, D, NW, MODE, PF>(p, b, h, part, L, pf, sm);
 }
 
@@ -636,7 +650,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_persistent(const DecodeP
     int items = 0;
     if (i < B) {
       const int L = max(0, min(p.context_lens[i], p.mbps * kBlockSize));
-      const int nb = (L + kBlockSize - 1) / kBlockSize;
+      const int nb = (L + kBlockSize - 1) / kBlockSize - window_block(L, p.window);
       int np = (nb + p.partition_blocks - 1) / p.partition_blocks;
       if (MODE != MODE_PARTIAL) np = max(np, 1);   // an empty context still writes zeros
       s_np[i] = np;
@@ -690,13 +704,13 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_persistent(const DecodeP
   int n = lo + static_cast<int>(blockIdx.x) / kXcds;
   if (n >= hi) return;
   locate(n, b, h, part);
-  item_prefetch<KVT, D, NW>(p, b, h, part, cur);
+  item_prefetch<KVT, D, NW>(p, b, h, part, s_len[b], cur);
   while (true) {
     // The next item's ids and q load while this item streams (the last item
     // prefetches itself again, so the load is never conditional).
     const int n2 = n + per_xcd;
     locate(min(n2, hi - 1), b2, h2, part2);
-    item_prefetch<KVT, D, NW>(p, b2, h2, part2, nxt);
+    item_prefetch<KVT, D, NW>(p, b2, h2, part2, s_len[b2], nxt);
     decode_item<KVT, D, NW, MODE, PF>(p, b, h, part, s_len[b], cur, sm);
     __syncthreads();   // the next item reuses the merge state
     if (n2 >= hi) break;
@@ -755,7 +769,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_stream(const DecodeParam
     if (i < B) {
       const int L = max(0, min(p.context_lens[i], p.mbps * kBlockSize));
       s_len[i] = L;
-      tiles = Hkv * ((L + kBlockSize - 1) / kBlockSize);
+      tiles = Hkv * ((L + kBlockSize - 1) / kBlockSize - window_block(L, p.window));
     }
     int x = tiles;
 #pragma unroll
@@ -794,7 +808,12 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_stream(const DecodeParam
   const int t_begin = static_cast<int>(static_cast<int64_t>(T) * w / R);
   const int t_end = static_cast<int>(static_cast<int64_t>(T) * (w + 1) / R);
 
-  // Tile t -> (sequence, kv head, block): last b with s_cum[b] <= t.
+  // An item's tiles are its blocks from the window's first block on:
+  // tile j of sequence b is block window_block(L_b) + j.
+  auto item_tiles = [&](int b) {
+    return (s_len[b] + kBlockSize - 1) / kBlockSize - window_block(s_len[b], p.window);
+  };
+  // Tile t -> (sequence, kv head, tile of the item): last b with s_cum[b] <= t.
   auto locate = [&](int t, int& b, int& h, int& j) {
     int lo_b = 0, hi_b = B;
     while (hi_b - lo_b > 1) {
@@ -803,33 +822,35 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_stream(const DecodeParam
       else hi_b = mid;
     }
     b = lo_b;
-    const int nb = (s_len[b] + kBlockSize - 1) / kBlockSize;
+    const int nt = item_tiles(b);
     const int local = t - s_cum[b];
-    h = local / nb;
-    j = local % nb;
+    h = local / nt;
+    j = local % nt;
   };
 
   int t = t_begin;
   int b, h, j0, b2, h2, j2;
   locate(t, b, h, j0);
   ItemPrefetch<KVT, D> cur, nxt;
-  meta_prefetch<KVT, D>(p, b, h, j0, 1, cur);
+  meta_prefetch<KVT, D>(p, b, h, window_block(s_len[b], p.window) + j0, 1, cur);
   WaveState<NT> st;
   while (true) {
     const int L = s_len[b];
-    const int nb = (L + kBlockSize - 1) / kBlockSize;
-    const int j1 = min(nb, j0 + (t_end - t));
+    const int lo = window_lo(L, p.window);
+    const int base = lo / kBlockSize;
+    const int nt = item_tiles(b);
+    const int j1 = min(nt, j0 + (t_end - t));
     const int t2 = t + (j1 - j0);
     // The next segment's ids and q load while this one streams (the last
     // segment prefetches its own last tile again: never a conditional load).
     locate(min(t2, t_end - 1), b2, h2, j2);
-    meta_prefetch<KVT, D>(p, b2, h2, j2, 1, nxt);
+    meta_prefetch<KVT, D>(p, b2, h2, window_block(s_len[b2], p.window) + j2, 1, nxt);
     st.reset();
-    attend_blocks<KVT, D, PF>(p, b, h, L, j0, 1, j1 - j0, cur.ids, cur.qop, st);
+    attend_blocks<KVT, D, PF>(p, b, h, L, lo, base + j0, 1, j1 - j0, cur.ids, cur.qop, st);
     const float l_sum = sum_over_groups(st.l);
     const float inv = 1.f / l_sum;
     if (r < G) {
-      if (j0 == 0 && j1 == nb) {   // the whole item: final output
+      if (j0 == 0 && j1 == nt) {   // the whole item: final output
         const size_t row = (static_cast<size_t>(b) * p.num_q_heads + h * G + r) * D;
 #pragma unroll
         for (int n = 0; n < NT; ++n) store4(p.out, row + 16 * n + 4 * g, p.out_dtype, st.o[n] * inv);
@@ -893,7 +914,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const ReduceParams p) {
   if (pair >= p.num_seqs * p.num_q_heads) return;
   const int b = pair / p.num_q_heads;
   const int L = max(0, min(p.context_lens[b], p.mbps * kBlockSize));
-  const int n = min((L + p.partition_size - 1) / p.partition_size, p.num_partitions);
+  const int origin = window_block(L, p.window) * kBlockSize;   // partition 0's first position
+  const int n = min((L - origin + p.partition_size - 1) / p.partition_size, p.num_partitions);
   float acc[D / 64];
   if (n > 0) {
     merge_partitions<D, false>(p.tmp_lse + static_cast<size_t>(pair) * p.num_partitions,

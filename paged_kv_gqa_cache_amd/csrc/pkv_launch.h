@@ -30,6 +30,7 @@ struct DecodeParams {
   int32_t* seq_tiles;          // [B + 1] tiles before each sequence (written by the kernel)
   int32_t num_workers;         // waves of the resident grid
   int32_t num_slots;           // B * Hkv + num_workers
+  int32_t window;              // sliding window in tokens (0: whole context)
 };
 
 struct ReduceParams {
@@ -41,6 +42,7 @@ struct ReduceParams {
   // Balanced schedule only.
   const int32_t* seq_tiles;
   int32_t num_kv_heads, num_workers, num_slots;
+  int32_t window;              // sliding window in tokens (0: whole context)
 };
 
 struct WriteParams {

@@ -19,20 +19,21 @@ def decode(w, pool, mode="split", partition_size=None, out_dtype=torch.float32, 
     q = q0 if q is None else q
     tables = t0 if tables is None else tables
     lens = l0 if lens is None else lens
+    W = w.spec.window
     if mode == "single":
-        return abi.paged_decode_attention(q, k, v, tables, lens, w.scale, scales, out_dtype=out_dtype)
+        return abi.paged_decode_attention(q, k, v, tables, lens, w.scale, scales, out_dtype=out_dtype, window=W)
     if mode == "balanced":
         ws = abi.balanced_workspace(q, k, tables)
         ws.fill_(0xFF)   # NaN bit patterns: a slot read before it is written shows up
         return abi.paged_decode_attention_balanced(q, k, v, tables, lens, w.scale, scales, ws,
-                                                   out_dtype=out_dtype)
+                                                   out_dtype=out_dtype, window=W)
     P = partition_size or w.spec.partition_size
     if mode == "fused":
         ws = abi.split_workspace(q, k, tables, P)
         return abi.paged_decode_attention_split(q, k, v, tables, lens, w.scale, scales, P, ws,
-                                                out_dtype=out_dtype)
+                                                out_dtype=out_dtype, window=W)
     tmp_out, tmp_lse = abi.alloc_partials(q, tables.shape[1], P)
-    abi.paged_decode_attention_partial(q, k, v, tables, lens, w.scale, scales, P, tmp_out, tmp_lse)
+    abi.paged_decode_attention_partial(q, k, v, tables, lens, w.scale, scales, P, tmp_out, tmp_lse, window=W)
     out = torch.empty(q.shape, dtype=out_dtype, device=device)
-    abi.paged_decode_attention_reduce(tmp_out, tmp_lse, lens, P, out, tables.shape[1])
+    abi.paged_decode_attention_reduce(tmp_out, tmp_lse, lens, P, out, tables.shape[1], window=W)
     return out

@@ -25,6 +25,7 @@ REDUCED = {
     "qwen25_1p5b": dict(num_seqs=4, lengths=("uniform", 1, 900)),
     "qwen25_7b_prefix": dict(num_seqs=16, lengths=("lognormal", 300, 1.0, 16, 3000)),
     "qwen25_7b_fp8": dict(num_seqs=3, lengths=("uniform", 1, 700)),
+    "gemma_sliding": dict(num_seqs=6, lengths=("uniform", 1, 900), window=200),
 }
 NAMES = list(REDUCED)
 
@@ -32,7 +33,7 @@ NAMES = list(REDUCED)
 def oracle_out(w, pool=None):
     k, v, sc = pool if pool is not None else oracle_pool(w)
     return ref.decode_attention(w.q, w.spec.q_dtype, k, v, w.spec.kv_dtype, w.block_tables,
-                                w.context_lens, w.scale, sc)
+                                w.context_lens, w.scale, sc, window=w.spec.window)
 
 
 def max_err(got: torch.Tensor, want: np.ndarray) -> float:
@@ -259,6 +260,63 @@ def test_empty_context_gives_zeros(mode):
     assert max_err(got, want) <= TOL
 
 
+# --------------------------------------------------------- sliding window ---
+
+@pytest.mark.parametrize("W", [1, 16, 17, 100, 512])
+@pytest.mark.parametrize("mode", MODES)
+def test_sliding_window_matches_oracle(W, mode):
+    """Windows shorter than, equal to a block, unaligned, and spanning
+    partitions; blocks before each window hold NaN, so a read outside it
+    would show."""
+    _announce("window", W, mode)
+    w = workloads.generate("gemma_sliding", num_seqs=5, lengths=("uniform", 1, 1500), window=W,
+                           num_q_heads=16, num_kv_heads=4)
+    assert max_err(decode(w, gpu_pool(w), mode, partition_size=64), oracle_out(w)) <= TOL
+
+
+def test_sliding_window_partials_match_oracle_partials():
+    _announce("window partials")
+    from paged_kv_gqa_cache_amd import abi
+    W, P = 300, 128
+    w = workloads.generate("gemma_sliding", num_seqs=6, lengths=("uniform", 1, 1200), window=W)
+    k, v, _ = oracle_pool(w)
+    pool = gpu_pool(w)
+    q, tables, lens = inputs(w)
+    tmp_out, tmp_lse = abi.alloc_partials(q, tables.shape[1], P)
+    tmp_out.fill_(float("nan"))
+    tmp_lse.fill_(float("nan"))
+    abi.paged_decode_attention_partial(q, pool[0], pool[1], tables, lens, w.scale, None, P, tmp_out, tmp_lse,
+                                       window=W)
+    S = tmp_out.shape[2]
+    o_ref, lse_ref = ref.decode_partials(w.q, "bf16", k, v, "bf16", w.block_tables, w.context_lens,
+                                         w.scale, P, S, window=W)
+    o_g, lse_g = tmp_out.cpu().numpy(), tmp_lse.cpu().numpy()
+    for b, L in enumerate(w.context_lens):
+        n = ref.num_partitions(L, P, W)
+        assert np.max(np.abs(o_g[b, :, :n] - o_ref[b, :, :n])) <= TOL
+        assert np.max(np.abs(lse_g[b, :, :n] - lse_ref[b, :, :n])) <= TOL
+        assert np.all(np.isnan(o_g[b, :, n:])) and np.all(np.isnan(lse_g[b, :, n:])), "wrote past its partitions"
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    abi.paged_decode_attention_reduce(tmp_out, tmp_lse, lens, P, out, tables.shape[1], window=W)
+    assert max_err(out, ref.merge_partials(o_ref, lse_ref, w.context_lens, P, W)) <= TOL
+
+
+def test_window_wider_than_every_context_equals_no_window_bitwise():
+    _announce("window wide")
+    w = workloads.generate("qwen25_1p5b", num_seqs=4, lengths=("uniform", 1, 600))
+    pool = gpu_pool(w)
+    base = decode(w, pool, "split")
+    from paged_kv_gqa_cache_amd import abi
+    q, tables, lens = inputs(w)
+    P = w.spec.partition_size
+    tmp_out, tmp_lse = abi.alloc_partials(q, tables.shape[1], P)
+    abi.paged_decode_attention_partial(q, pool[0], pool[1], tables, lens, w.scale, None, P, tmp_out, tmp_lse,
+                                       window=100000)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    abi.paged_decode_attention_reduce(tmp_out, tmp_lse, lens, P, out, tables.shape[1], window=100000)
+    assert torch.equal(out, base)
+
+
 # ------------------------------------------------------- balanced schedule ---
 
 @pytest.mark.parametrize("lengths", [("uniform", 1, 40), ("lognormal", 200, 1.5, 1, 6000)])
@@ -309,7 +367,8 @@ def test_balanced_rejects_too_many_sequences():
 FULL_SAMPLE = 6
 
 
-@pytest.mark.parametrize("name", ["smollm2_360m", "qwen25_1p5b", "qwen25_7b_prefix", "qwen25_7b_fp8"])
+@pytest.mark.parametrize("name", ["smollm2_360m", "qwen25_1p5b", "qwen25_7b_prefix", "qwen25_7b_fp8",
+                                  "gemma_sliding"])
 def test_full_size_sampled_sequences(name):
     """Each workload at its full size, in the split configuration the benchmark
     times; the oracle checks a sample of sequences (the longest, the shortest
