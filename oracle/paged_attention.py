@@ -155,6 +155,26 @@ def kv_cache_write_e4m3_blocks(k_cache, v_cache, kv_scales, k_blocks, v_blocks,
         kv_scales[1, ids[sl]] = vs
 
 
+def copy_blocks(k_cache, v_cache, block_mapping, kv_scales=None) -> None:
+    """Copy whole blocks inside the pool: for each pair (src, dst) of
+    ``block_mapping`` [n, 2], block dst's K and V tiles of every kv head, and
+    for an E4M3 pool its K and V scales, become bit copies of block src's.
+    Every source is read before any destination is written.
+
+    ("rvLLM: High-performance LLM inference in Rust", section "CUDA Kernels",
+    row "Block Copy": KV cache block copy for beam search; section
+    "Architecture": the block manager's copy-on-write.)
+    """
+    m = np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2)
+    src, dst = m[:, 0], m[:, 1]
+    k_src, v_src = k_cache[src].copy(), v_cache[src].copy()
+    k_cache[dst] = k_src
+    v_cache[dst] = v_src
+    if kv_scales is not None:
+        s_src = kv_scales[:, src].copy()
+        kv_scales[:, dst] = s_src
+
+
 # ---------------------------------------------------------------- gather ---
 
 def window_start(context_len: int, window: int) -> int:

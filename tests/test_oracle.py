@@ -479,3 +479,47 @@ def test_window_generator_counts_only_window_bytes():
     per_tok = 2 * w.spec.num_kv_heads * w.spec.head_dim * 2
     assert workloads.kv_bytes(w, unique=False) == int(np.minimum(L, 40).sum()) * per_tok
     assert workloads.kv_bytes(w, unique=True) == int(np.minimum(L, 40).sum()) * per_tok
+
+
+# ------------------------------------------------------------ block copy ---
+
+def test_copy_blocks_copies_bits_of_every_head_and_nothing_else():
+    w = small("qwen25_7b_fp8", num_seqs=3, lengths=("uniform", 20, 200))
+    k, v, sc = oracle_pool(w)
+    k0, v0, s0 = k.copy(), v.copy(), sc.copy()
+    used = sorted(set(int(x) for x in w.fill_blocks))
+    free = [i for i in range(w.num_blocks) if i not in set(used)]
+    pairs = [(used[0], free[0]), (used[2], free[1]), (used[1], free[2])]
+    ref.copy_blocks(k, v, pairs, sc)
+    for s_, d_ in pairs:
+        for h in range(w.spec.num_kv_heads):
+            assert k[d_, h].tobytes() == k0[s_, h].tobytes() and v[d_, h].tobytes() == v0[s_, h].tobytes()
+            assert sc[0, d_, h] == s0[0, s_, h] and sc[1, d_, h] == s0[1, s_, h]
+    others = [i for i in range(w.num_blocks) if i not in {d for _, d in pairs}]
+    assert np.array_equal(k[others], k0[others]) and np.array_equal(v[others], v0[others])
+    assert np.array_equal(sc[:, others], s0[:, others])
+
+
+def test_forked_sequence_reads_the_same_until_its_copy_diverges():
+    """Copy-on-write fork: a second table row whose last block is a copy of the
+    first sequence's last block decodes identically; writing a different next
+    token into the copy changes only the fork."""
+    w = small("qwen25_1p5b", num_seqs=2, lengths=("fixed", 37))
+    k, v, _ = oracle_pool(w)
+    free = [i for i in range(w.num_blocks) if i not in set(int(x) for x in w.block_tables.ravel())]
+    last = int(w.block_tables[0, 2])
+    ref.copy_blocks(k, v, [(last, free[0])])
+    tables = w.block_tables.copy()
+    tables[1] = tables[0]
+    tables[1, 2] = free[0]
+    q = np.repeat(w.q[:1], 2, axis=0)
+    out = ref.decode_attention(q, "f16", k, v, "f16", tables, np.array([37, 37], np.int32), w.scale)
+    assert np.array_equal(out[0], out[1])
+    rng = np.random.default_rng(5)
+    nk = workloads.round_to(rng.standard_normal((1, 2, 128), dtype=np.float32), "f16")
+    nv = workloads.round_to(rng.standard_normal((1, 2, 128), dtype=np.float32), "f16")
+    ref.kv_cache_write(k, v, nk, nv, np.array([free[0] * 16 + 5], np.int64), "f16")
+    out2 = ref.decode_attention(q, "f16", k, v, "f16", tables, np.array([38, 38], np.int32), w.scale)
+    base = ref.decode_attention(q[:1], "f16", k, v, "f16", tables[:1], np.array([37], np.int32), w.scale)
+    assert np.array_equal(out[0], base[0])                  # the original never saw the fork's token
+    assert not np.array_equal(out2[1], out[1])              # the fork did
