@@ -152,6 +152,26 @@ int kv_cache_quantize_e4m3(const float* k_src, const float* v_src, const int32_t
                            void* v_cache, float* kv_scales, const pkv_desc* desc, void* stream);
 
 /*
+ * kv_cache_copy_blocks - copy whole blocks inside the pool, for
+ * copy-on-write forks such as beam search ("rvLLM: High-performance LLM
+ * inference in Rust", section "CUDA Kernels", row "Block Copy"; section
+ * "Architecture": the block manager's copy-on-write and prefix sharing).
+ *
+ *   block_mapping  int32 [num_pairs][2]: (src, dst) block ids
+ *   num_pairs      0 .. 65535
+ *   k_cache, v_cache  the pool in desc->kv_dtype (any of the four)
+ *   kv_scales      fp32 [2][NB][Hkv] for an e4m3 pool (its K and V scales
+ *                  are copied too), else NULL
+ * Block dst's K and V tiles of every kv head become bit copies of block
+ * src's.  Reads desc->num_kv_heads, head_dim, num_blocks and kv_dtype only.
+ * A pair naming a block outside [0, num_blocks) is skipped.  No block may
+ * be a destination twice, or both a source and a destination, in one call
+ * (the copies run in parallel).
+ */
+int kv_cache_copy_blocks(const int32_t* block_mapping, int32_t num_pairs, void* k_cache,
+                         void* v_cache, float* kv_scales, const pkv_desc* desc, void* stream);
+
+/*
  * paged_decode_attention - one decode step of attention for every sequence
  * in one pass: out[b][i] = softmax(q[b][i] . K_b^T * scale) V_b, where K_b,
  * V_b are the first context_lens[b] tokens of sequence b gathered through

@@ -51,6 +51,7 @@ def _load():
     sigs = {
         "kv_cache_write": (ctypes.c_int, [P, P, P, I64, P, P, D, P]),
         "kv_cache_quantize_e4m3": (ctypes.c_int, [P, P, P, P, I32, P, P, P, D, P]),
+        "kv_cache_copy_blocks": (ctypes.c_int, [P, I32, P, P, P, D, P]),
         "paged_decode_attention": (ctypes.c_int, [P, P, P, P, P, F, P, P, D, P]),
         "paged_decode_attention_partial": (ctypes.c_int, [P, P, P, P, P, F, P, I32, P, P, D, P]),
         "paged_decode_attention_reduce": (ctypes.c_int, [P, P, P, I32, P, D, P]),
@@ -70,7 +71,7 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("kv_cache_write", "kv_cache_quantize_e4m3", "paged_decode_attention",
+EXPORTED = ("kv_cache_write", "kv_cache_quantize_e4m3", "kv_cache_copy_blocks", "paged_decode_attention",
             "paged_decode_attention_partial", "paged_decode_attention_reduce",
             "paged_decode_attention_split", "paged_decode_split_workspace_bytes",
             "paged_decode_attention_balanced", "paged_decode_balanced_workspace_bytes",
@@ -148,6 +149,18 @@ def kv_cache_quantize_e4m3(k_src, v_src, block_ids, valid_tokens, k_cache, v_cac
     _check("kv_cache_quantize_e4m3", _lib.kv_cache_quantize_e4m3(
         _ptr(k_src), _ptr(v_src), _ptr(block_ids), _ptr(valid_tokens), n, _ptr(k_cache),
         _ptr(v_cache), _ptr(kv_scales), ctypes.byref(desc), _stream(stream)))
+
+
+def kv_cache_copy_blocks(block_mapping, k_cache, v_cache, kv_scales=None, stream=None) -> None:
+    """Copy blocks inside the pool: block_mapping int32 [n, 2] of (src, dst) pairs."""
+    n = int(block_mapping.shape[0])
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    D = k_cache.shape[2] // BLOCK_SIZE
+    code = _code(k_cache)
+    desc = make_desc(0, Hkv, Hkv, D, NB, 1, code, code, code)
+    _check("kv_cache_copy_blocks", _lib.kv_cache_copy_blocks(
+        _ptr(block_mapping), n, _ptr(k_cache), _ptr(v_cache), _ptr(kv_scales), ctypes.byref(desc),
+        _stream(stream)))
 
 
 def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,

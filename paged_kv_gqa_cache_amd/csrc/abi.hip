@@ -234,6 +234,29 @@ int kv_cache_quantize_e4m3(const float* k_src, const float* v_src, const int32_t
                     "kv_cache_quantize_e4m3 launch");
 }
 
+int kv_cache_copy_blocks(const int32_t* block_mapping, int32_t num_pairs, void* k_cache, void* v_cache,
+                         float* kv_scales, const pkv_desc* desc, void* stream) {
+  if (int e = check_desc(desc, false)) return e;
+  const int e_bytes = elem_bytes(desc->kv_dtype);
+  if (e_bytes == 0) return fail(PKV_ERR_UNSUPPORTED, "kv_dtype %d", desc->kv_dtype);
+  if (num_pairs < 0 || num_pairs > 65535) return fail(PKV_ERR_INVALID_ARG, "num_pairs must be in [0, 65535]");
+  if (desc->kv_dtype == PKV_E4M3 && !kv_scales) return fail(PKV_ERR_INVALID_ARG, "e4m3 cache needs kv_scales");
+  if (desc->kv_dtype != PKV_E4M3 && kv_scales)
+    return fail(PKV_ERR_INVALID_ARG, "kv_scales given for a non-e4m3 cache");
+  if (num_pairs == 0) return ok();
+  if (!block_mapping || !k_cache || !v_cache) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  pkv::CopyParams p{};
+  p.block_mapping = block_mapping;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.kv_scales = kv_scales;
+  p.block_bytes = static_cast<int64_t>(desc->num_kv_heads) * 16 * desc->head_dim * e_bytes;
+  p.num_pairs = num_pairs;
+  p.num_blocks = desc->num_blocks;
+  p.num_kv_heads = desc->num_kv_heads;
+  return hip_status(pkv::launch_copy_blocks(p, static_cast<hipStream_t>(stream)), "kv_cache_copy_blocks launch");
+}
+
 int paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, const int32_t* context_lens, float scale,
                            const float* kv_scales, void* out, const pkv_desc* desc, void* stream) {

@@ -9,7 +9,12 @@
 //    "Projects", row 05: E4M3 storage, page scales; "rvLLM: ...", "CUDA
 //    Kernels", row "FP8 KV Cache": per-head scaling).
 //
-// Both are pure data movement plus index arithmetic; the tile layouts are
+//  * copy_blocks_kernel: whole blocks copied inside the pool, for
+//    copy-on-write forks ("rvLLM: ...", "CUDA Kernels", row "Block Copy":
+//    KV cache block copy for beam search; section "Architecture": the block
+//    manager's copy-on-write).
+//
+// All are pure data movement plus index arithmetic; the tile layouts are
 // the ones documented in pagedkv.h.
 #include "pkv_common.h"
 #include "pkv_launch.h"
@@ -123,6 +128,37 @@ __global__ __launch_bounds__(128) void quantize_e4m3_kernel(const QuantParams p)
   st16(cache + tile + byte, u32x4{w[0], w[1], w[2], w[3]});
   if (tid == 0)
     p.kv_scales[((is_v ? static_cast<size_t>(p.num_blocks) : 0) + blk) * p.num_kv_heads + h] = scale;
+}
+
+// One thread per 16-byte chunk of a block (a block's Hkv tiles are one
+// contiguous run), grid (chunks / 256, pairs, K-or-V).  Pairs naming a block
+// outside the pool are skipped.  The first threads of each (pair, K-or-V)
+// (blockIdx.x = 0) also copy that block's Hkv scales of an E4M3 pool.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(const CopyParams p) {
+  const int pair = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const int src = p.block_mapping[2 * pair];
+  const int dst = p.block_mapping[2 * pair + 1];
+  if (src < 0 || src >= p.num_blocks || dst < 0 || dst >= p.num_blocks) return;
+  char* cache = static_cast<char*>(is_v ? p.v_cache : p.k_cache);
+  const int64_t chunk = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (chunk < p.block_bytes / 16) {
+    const u32x4 x = ld16(cache + static_cast<size_t>(src) * p.block_bytes + chunk * 16);
+    st16(cache + static_cast<size_t>(dst) * p.block_bytes + chunk * 16, x);
+  }
+  if (p.kv_scales != nullptr && blockIdx.x == 0) {
+    float* sc = p.kv_scales + (is_v ? static_cast<size_t>(p.num_blocks) * p.num_kv_heads : 0);
+    for (int h = threadIdx.x; h < p.num_kv_heads; h += 256)
+      sc[static_cast<size_t>(dst) * p.num_kv_heads + h] = sc[static_cast<size_t>(src) * p.num_kv_heads + h];
+  }
+}
+
+hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream) {
+  if (p.num_pairs == 0) return hipSuccess;
+  const int64_t chunks = p.block_bytes / 16;
+  const dim3 grid(static_cast<unsigned>((chunks + 255) / 256), static_cast<unsigned>(p.num_pairs), 2), block(256);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, block, 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_kv_write(const WriteParams& p, hipStream_t stream) {

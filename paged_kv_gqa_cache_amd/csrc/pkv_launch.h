@@ -66,6 +66,15 @@ struct QuantParams {
   int32_t num_src_blocks, num_kv_heads, head_dim, num_blocks;
 };
 
+struct CopyParams {
+  const int32_t* block_mapping;  // [num_pairs][2]: (src, dst)
+  void* k_cache;
+  void* v_cache;
+  float* kv_scales;              // [2][NB][Hkv] for an e4m3 pool, else null
+  int64_t block_bytes;           // Hkv * 16 * D * elem bytes (a multiple of 16)
+  int32_t num_pairs, num_blocks, num_kv_heads;
+};
+
 // Each returns hipSuccess or the launch error.
 // mode: 0 one pass to out, 1 partials to the workspace, 2 partials merged
 // in-kernel by the last partition of each (sequence, kv head).
@@ -79,5 +88,6 @@ hipError_t launch_stream(const DecodeParams& p, int kv_dtype, int head_dim, hipS
 hipError_t launch_stream_merge(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_kv_write(const WriteParams& p, hipStream_t stream);
 hipError_t launch_quantize_e4m3(const QuantParams& p, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
 
 }  // namespace pkv

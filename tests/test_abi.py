@@ -149,3 +149,15 @@ def test_balanced_rejects_before_touching_the_device():
     assert balanced(desc(max_blocks_per_seq=1 << 20, num_seqs=2048, num_kv_heads=2)) == INVALID
     assert balanced(desc(q_dtype=abi.PKV_BF16)) == UNSUPPORTED
     assert balanced(desc(num_seqs=0), ptr=None) == OK
+
+
+def test_copy_blocks_validates_before_touching_the_device():
+    lib = abi.lib()
+    d = desc()
+    assert lib.kv_cache_copy_blocks(None, 0, None, None, None, ctypes.byref(d), None) == OK
+    assert lib.kv_cache_copy_blocks(FAKE, -1, FAKE, FAKE, None, ctypes.byref(d), None) == INVALID
+    assert lib.kv_cache_copy_blocks(None, 2, FAKE, FAKE, None, ctypes.byref(d), None) == INVALID
+    assert lib.kv_cache_copy_blocks(FAKE, 2, FAKE, FAKE, FAKE, ctypes.byref(d), None) == INVALID   # scales, 16-bit
+    d8 = desc(kv_dtype=abi.PKV_E4M3)
+    assert lib.kv_cache_copy_blocks(FAKE, 2, FAKE, FAKE, None, ctypes.byref(d8), None) == INVALID  # e4m3, no scales
+    assert lib.kv_cache_copy_blocks(FAKE, 2, FAKE, FAKE, None, ctypes.byref(desc(kv_dtype=9)), None) == UNSUPPORTED

@@ -400,3 +400,81 @@ def test_full_size_sampled_sequences(name):
     assert np.all(np.isfinite(got)) and np.all(np.isfinite(fused)) and np.all(np.isfinite(bal))
     assert float(np.max(np.abs(fused - got))) <= TOL
     assert float(np.max(np.abs(bal - got))) <= TOL
+
+
+# ------------------------------------------------------------ block copy ---
+
+@pytest.mark.parametrize("name", ["tiny", "qwen25_7b_prefix", "qwen25_7b_fp8", "smollm2_360m"])
+def test_copy_blocks_is_bit_exact(name):
+    """Pairs from used blocks into free ones (and one pair naming a block past
+    the pool, which is skipped): every byte of the pool, and the E4M3 scales,
+    equal the oracle's copy."""
+    _announce("copy blocks", name)
+    from paged_kv_gqa_cache_amd import abi
+    w = workloads.generate(name, **REDUCED[name]) if name != "tiny" else workloads.generate(name)
+    k_o, v_o, s_o = oracle_pool(w)
+    k_g, v_g, s_g = gpu_pool(w)
+    used = sorted(set(int(x) for x in w.fill_blocks))
+    free = [i for i in range(w.num_blocks) if i not in set(used)]
+    n = min(len(used), len(free), 7)
+    pairs = [(used[i], free[i]) for i in range(n)]
+    ref.copy_blocks(k_o, v_o, pairs, s_o)
+    mapping = torch.tensor(pairs + [(used[0], w.num_blocks + 3)], dtype=torch.int32, device="cuda")
+    abi.kv_cache_copy_blocks(mapping, k_g, v_g, s_g)
+    torch.cuda.synchronize()
+    kv = w.spec.kv_dtype
+    assert np.array_equal(to_raw(k_g, kv), k_o) and np.array_equal(to_raw(v_g, kv), v_o)
+    if s_o is not None:
+        assert np.array_equal(s_g.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+
+
+def test_forked_beam_after_copy_and_write_matches_oracle():
+    """Copy-on-write fork on the GPU: each sequence's partly filled last block
+    is copied for a second beam, each beam gets a different next token, and
+    both beams decode as the oracle says."""
+    _announce("beam fork")
+    from paged_kv_gqa_cache_amd import abi
+    w = workloads.generate("qwen25_1p5b", num_seqs=4, lengths=("uniform", 20, 300))
+    k_o, v_o, _ = oracle_pool(w)
+    k_g, v_g, _ = gpu_pool(w)
+    B = w.spec.num_seqs
+    used = set(int(x) for x in w.block_tables.ravel() if x >= 0)
+    free = [i for i in range(w.num_blocks) if i not in used][:B]
+    L = w.context_lens.astype(np.int64)
+    last = w.block_tables[np.arange(B), (L - 1) // 16].astype(np.int64)
+    # Fork only where the new token lands in the same block as the last one.
+    pairs = [(int(last[b]), free[b]) for b in range(B)]
+    ref.copy_blocks(k_o, v_o, pairs)
+    abi.kv_cache_copy_blocks(torch.tensor(pairs, dtype=torch.int32, device="cuda"), k_g, v_g)
+    tables = np.concatenate([w.block_tables, w.block_tables], axis=0)
+    for b in range(B):
+        tables[B + b, (L[b] - 1) // 16] = free[b]
+    # the next token of every beam: position L, slot in the beam's own block (a new block if L % 16 == 0)
+    rng = np.random.default_rng(11)
+    Hkv, D = w.spec.num_kv_heads, w.spec.head_dim
+    extra = [i for i in range(w.num_blocks) if i not in used and i not in free]
+    slots = []
+    for r in range(2 * B):
+        b = r % B
+        pos = int(L[b])
+        if pos % 16 == 0:
+            blk = extra.pop(0)
+            tables_row_len = tables.shape[1]
+            if pos // 16 >= tables_row_len:
+                tables = np.concatenate([tables, np.full((2 * B, 1), -1, np.int32)], axis=1)
+            tables[r, pos // 16] = blk
+        else:
+            blk = int(tables[r, pos // 16])
+        slots.append(blk * 16 + pos % 16)
+    slots = np.array(slots, np.int64)
+    nk = workloads.round_to(rng.standard_normal((2 * B, Hkv, D), dtype=np.float32), "f16")
+    nv = workloads.round_to(rng.standard_normal((2 * B, Hkv, D), dtype=np.float32), "f16")
+    ref.kv_cache_write(k_o, v_o, nk, nv, slots, "f16")
+    abi.kv_cache_write(to_dev(nk, "f16"), to_dev(nv, "f16"), torch.from_numpy(slots).cuda(), k_g, v_g)
+    lens = np.concatenate([L + 1, L + 1]).astype(np.int32)
+    q = np.concatenate([w.q, w.q], axis=0)
+    want = ref.decode_attention(q, "f16", k_o, v_o, "f16", tables, lens, w.scale)
+    got = abi.paged_decode_attention(to_dev(q, "f16"), k_g, v_g, torch.from_numpy(tables).cuda(),
+                                     torch.from_numpy(lens).cuda(), w.scale)
+    assert max_err(got, want) <= TOL
+    assert not np.allclose(want[:B], want[B:])   # the beams did diverge
