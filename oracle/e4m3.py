@@ -115,6 +115,40 @@ def quantize_blocks(x_blocks: np.ndarray, valid_tokens: np.ndarray):
     return codes, scales
 
 
+def append_token(block_codes: np.ndarray, scale, offset: int, x: np.ndarray):
+    """One step of quantise-on-append for one (block, kv head), K or V.
+
+    ``block_codes``: uint8 [16, D], the block's codes in slot order (slots at
+    or past ``offset`` are ignored); ``scale``: the block's current fp32 scale
+    (ignored when ``offset`` is 0); ``x``: float32 [D], the token going to slot
+    ``offset``.  Returns ``(codes, scale)`` after the step.
+
+    The pages fix a scale per page and head but no append policy.  Reading
+    taken (listed in the design doc): the block keeps the bulk quantiser's
+    invariant scale = fp32(amax / 448) over its tokens so far.  The token's
+    own s = fp32(amax(|x|) / 448); a block's first token sets the scale (1 if
+    s is 0); a later token with s above the current scale grows it to s, and
+    the block's earlier codes are re-encoded: value = fp32(decode(c) *
+    old scale), code = nearest-even E4M3 of clamp(fp32(value / s)).  The token
+    itself is then encoded against the (new) scale like the bulk quantiser.
+    Every rounding step is fp32, as on the GPU.
+    """
+    codes = np.array(block_codes, dtype=np.uint8, copy=True)
+    x = np.asarray(x, dtype=np.float32)
+    s_tok = np.float32(np.max(np.abs(x))) / np.float32(E4M3_MAX)
+    if offset == 0:
+        s = s_tok if s_tok > 0 else np.float32(1)
+    else:
+        s = np.float32(scale)
+        if s_tok > s:
+            old = decode(codes[:offset]).astype(np.float32) * s              # fp32 product
+            codes[:offset] = encode(np.clip((old / s_tok).astype(np.float32).astype(np.float64),
+                                            -E4M3_MAX, E4M3_MAX))
+            s = s_tok
+    codes[offset] = encode(np.clip((x / s).astype(np.float32).astype(np.float64), -E4M3_MAX, E4M3_MAX))
+    return codes, np.float32(s)
+
+
 def storage_saving(block_size: int, head_dim: int, scale_bytes: int = 4,
                    separate_kv_scales: bool = True) -> float:
     """Fraction of KV bytes saved by E4M3 + fp32 page scales versus fp16.

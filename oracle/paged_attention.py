@@ -125,6 +125,28 @@ def kv_cache_write(k_cache, v_cache, k_raw, v_raw, slot_mapping, dtype: str) -> 
     v_cache[blk[:, None, None], heads, vidx[off][:, None, :]] = np.asarray(v_raw)[keep]
 
 
+def kv_cache_append_e4m3(k_cache, v_cache, kv_scales, k_new, v_new, slot_mapping) -> None:
+    """Quantise-on-append of new tokens into an E4M3 pool (``e4m3.append_token``
+    per token, kv head, and K or V).
+
+    ``k_new``/``v_new``: float32 [T, Hkv, D]; ``slot_mapping``: [T], negative
+    skips.  Tokens are taken in order; the write rule needs at most one token
+    per block per call, which the GPU path requires too.
+    """
+    head_dim = k_cache.shape[-1] // BLOCK_SIZE
+    kidx = k_tile_index(head_dim, "e4m3")          # [16, D] tile positions
+    vidx = v_tile_index(head_dim, "e4m3")
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0:
+            continue
+        blk, off = int(slot // BLOCK_SIZE), int(slot % BLOCK_SIZE)
+        for h in range(k_cache.shape[1]):
+            for which, cache, idx, x in ((0, k_cache, kidx, k_new), (1, v_cache, vidx, v_new)):
+                codes, sc = e4m3.append_token(cache[blk, h][idx], kv_scales[which, blk, h], off, x[t, h])
+                cache[blk, h][idx] = codes
+                kv_scales[which, blk, h] = sc
+
+
 def kv_cache_write_e4m3_blocks(k_cache, v_cache, kv_scales, k_blocks, v_blocks,
                                block_ids, valid_tokens) -> None:
     """Quantise whole blocks of fp32 K/V to E4M3 and store codes and scales.

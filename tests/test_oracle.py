@@ -523,3 +523,79 @@ def test_forked_sequence_reads_the_same_until_its_copy_diverges():
     base = ref.decode_attention(q[:1], "f16", k, v, "f16", tables[:1], np.array([37], np.int32), w.scale)
     assert np.array_equal(out[0], base[0])                  # the original never saw the fork's token
     assert not np.array_equal(out2[1], out[1])              # the fork did
+
+
+# --------------------------------------------------- E4M3 quantise-on-append ---
+
+def _grow_free_block(D=64, n=12, seed=3, lead=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, D), dtype=np.float32)
+    if lead:   # the first token holds the block's largest magnitude: no growth
+        x[0, 0] = np.float32(1.5) * np.max(np.abs(x))
+    return x
+
+
+def test_append_without_growth_equals_the_bulk_quantiser():
+    x = _grow_free_block()
+    codes, s = np.zeros((16, 64), np.uint8), np.float32(0)
+    for t in range(len(x)):
+        codes, s = e4m3.append_token(codes, s, t, x[t])
+    blk = np.zeros((1, 16, 1, 64), np.float32)
+    blk[0, :len(x), 0] = x
+    bc, bs = e4m3.quantize_blocks(blk, np.array([len(x)]))
+    assert s == bs[0, 0]
+    assert np.array_equal(codes[:len(x)], bc[0, :len(x), 0])
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_append_scale_is_fp32_amax_over_448_and_error_is_bounded(seed):
+    """Rising magnitudes force several rescales: the scale stays
+    fp32(amax / 448) over the tokens so far, and every stored value stays
+    within one E4M3 rounding per (re)encoding of its token."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((16, 64), dtype=np.float32) * np.linspace(0.1, 3.0, 16, dtype=np.float32)[:, None]
+    codes, s = np.zeros((16, 64), np.uint8), np.float32(0)
+    encodings = np.zeros(16, int)
+    for t in range(16):
+        prev = s
+        codes, s = e4m3.append_token(codes, s, t, x[t])
+        amax = np.max(np.abs(x[:t + 1]))
+        assert s == np.float32(amax) / np.float32(448)
+        if t > 0 and s != prev:
+            encodings[:t] += 1
+        encodings[t] += 1
+    got = e4m3.decode(codes) * np.float64(s)
+    err = np.abs(got - x.astype(np.float64))
+    bound = encodings[:, None] * (2.0 ** -4 * np.abs(x.astype(np.float64)) * 1.01 + 2.0 ** -10 * float(s) * 1.01)
+    assert np.all(err <= bound + 1e-30)
+    assert np.sum(encodings > 1) > 0   # the test really re-encoded
+
+
+def test_append_of_a_zero_token_to_a_fresh_block_has_scale_one():
+    codes, s = e4m3.append_token(np.full((16, 64), 0x55, np.uint8), np.float32(7), 0, np.zeros(64, np.float32))
+    assert s == 1 and np.all(codes[0] == 0) and np.all(codes[1:] == 0x55)
+
+
+def test_pool_append_matches_per_head_steps_and_leaves_other_slots():
+    w = small("qwen25_7b_fp8", num_seqs=3, lengths=("uniform", 10, 60))
+    k, v, sc = oracle_pool(w)
+    k0, v0, s0 = k.copy(), v.copy(), sc.copy()
+    rng = np.random.default_rng(4)
+    L = w.context_lens.astype(np.int64)
+    slots = (w.block_tables[np.arange(3), L // 16].astype(np.int64) * 16 + L % 16)
+    kn = rng.standard_normal((3, 4, 128), dtype=np.float32) * 4
+    vn = rng.standard_normal((3, 4, 128), dtype=np.float32)
+    ok = w.block_tables[np.arange(3), L // 16] >= 0
+    slots = np.where(ok, slots, -1)
+    ref.kv_cache_append_e4m3(k, v, sc, kn, vn, slots)
+    kidx = ref.k_tile_index(128, "e4m3")
+    for t, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        blk, off = slot // 16, slot % 16
+        for h in range(4):
+            c, s = e4m3.append_token(k0[blk, h][kidx], s0[0, blk, h], off, kn[t, h])
+            assert np.array_equal(k[blk, h][kidx], c) and sc[0, blk, h] == s
+    touched = set(int(s // 16) for s in slots if s >= 0)
+    others = [i for i in range(w.num_blocks) if i not in touched]
+    assert np.array_equal(k[others], k0[others]) and np.array_equal(sc[:, others], s0[:, others])
