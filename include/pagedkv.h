@@ -123,7 +123,8 @@ typedef struct pkv_desc {
  *   k_cache, v_cache  the pool, layout above; only the named slots change
  * Bitwise copy.  Two tokens naming the same slot: which one lands is
  * unspecified.  An e4m3 cache returns PKV_ERR_UNSUPPORTED (use
- * kv_cache_quantize_e4m3 for whole blocks).
+ * kv_cache_append_e4m3 for new tokens, kv_cache_quantize_e4m3 for whole
+ * blocks).
  */
 int kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
                    int64_t num_tokens, void* k_cache, void* v_cache,
@@ -150,6 +151,31 @@ int kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
 int kv_cache_quantize_e4m3(const float* k_src, const float* v_src, const int32_t* block_ids,
                            const int32_t* valid_tokens, int32_t num_src_blocks, void* k_cache,
                            void* v_cache, float* kv_scales, const pkv_desc* desc, void* stream);
+
+/*
+ * kv_cache_append_e4m3 - write each new token's K and V into an e4m3 pool,
+ * quantising on append with one fp32 scale per (block, kv head) for K and
+ * one for V (the per-page, per-head scaling of "LLM Serving Kernels",
+ * section "Projects", row 05, and "rvLLM: High-performance LLM inference in
+ * Rust", section "CUDA Kernels", row "FP8 KV Cache", applied to the decode
+ * step's new token).
+ *
+ *   k, v          fp32 [num_tokens][Hkv][D]
+ *   slot_mapping  int64 [num_tokens]; negative skips the token
+ *   k_cache, v_cache  e4m3 pool (desc->kv_dtype must be PKV_E4M3)
+ *   kv_scales     fp32 [2][NB][Hkv], read and updated
+ * Per (token, kv head), for K and for V, every step in fp32: s =
+ * amax(|x|) / 448.  In slot 0 of a block the token sets the block's scale to
+ * s (1 if s is 0).  In a later slot, if s exceeds the stored scale, the
+ * block's earlier slots are re-encoded as code(clamp(decode(c) * old / s))
+ * and the scale becomes s; so the scale is always fp32(amax / 448) over the
+ * block's tokens, as kv_cache_quantize_e4m3 makes it.  The token's code is
+ * code(clamp(x / scale)), nearest-even OCP E4M3.  At most one token per
+ * block per call.  Slots past the token in its block are left as they are.
+ */
+int kv_cache_append_e4m3(const float* k, const float* v, const int64_t* slot_mapping,
+                         int64_t num_tokens, void* k_cache, void* v_cache, float* kv_scales,
+                         const pkv_desc* desc, void* stream);
 
 /*
  * kv_cache_copy_blocks - copy whole blocks inside the pool, for

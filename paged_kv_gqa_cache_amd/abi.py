@@ -52,6 +52,7 @@ def _load():
         "kv_cache_write": (ctypes.c_int, [P, P, P, I64, P, P, D, P]),
         "kv_cache_quantize_e4m3": (ctypes.c_int, [P, P, P, P, I32, P, P, P, D, P]),
         "kv_cache_copy_blocks": (ctypes.c_int, [P, I32, P, P, P, D, P]),
+        "kv_cache_append_e4m3": (ctypes.c_int, [P, P, P, I64, P, P, P, D, P]),
         "paged_decode_attention": (ctypes.c_int, [P, P, P, P, P, F, P, P, D, P]),
         "paged_decode_attention_partial": (ctypes.c_int, [P, P, P, P, P, F, P, I32, P, P, D, P]),
         "paged_decode_attention_reduce": (ctypes.c_int, [P, P, P, I32, P, D, P]),
@@ -71,7 +72,8 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("kv_cache_write", "kv_cache_quantize_e4m3", "kv_cache_copy_blocks", "paged_decode_attention",
+EXPORTED = ("kv_cache_write", "kv_cache_quantize_e4m3", "kv_cache_append_e4m3", "kv_cache_copy_blocks",
+            "paged_decode_attention",
             "paged_decode_attention_partial", "paged_decode_attention_reduce",
             "paged_decode_attention_split", "paged_decode_split_workspace_bytes",
             "paged_decode_attention_balanced", "paged_decode_balanced_workspace_bytes",
@@ -149,6 +151,15 @@ def kv_cache_quantize_e4m3(k_src, v_src, block_ids, valid_tokens, k_cache, v_cac
     _check("kv_cache_quantize_e4m3", _lib.kv_cache_quantize_e4m3(
         _ptr(k_src), _ptr(v_src), _ptr(block_ids), _ptr(valid_tokens), n, _ptr(k_cache),
         _ptr(v_cache), _ptr(kv_scales), ctypes.byref(desc), _stream(stream)))
+
+
+def kv_cache_append_e4m3(k, v, slot_mapping, k_cache, v_cache, kv_scales, stream=None) -> None:
+    """fp32 k, v [T, Hkv, D] quantised on append into their slots of an e4m3 pool."""
+    T, Hkv, D = k.shape
+    desc = make_desc(0, Hkv, Hkv, D, k_cache.shape[0], 1, PKV_F32, PKV_E4M3, PKV_F32)
+    _check("kv_cache_append_e4m3", _lib.kv_cache_append_e4m3(
+        _ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache), _ptr(kv_scales),
+        ctypes.byref(desc), _stream(stream)))
 
 
 def kv_cache_copy_blocks(block_mapping, k_cache, v_cache, kv_scales=None, stream=None) -> None:

@@ -234,6 +234,29 @@ int kv_cache_quantize_e4m3(const float* k_src, const float* v_src, const int32_t
                     "kv_cache_quantize_e4m3 launch");
 }
 
+int kv_cache_append_e4m3(const float* k, const float* v, const int64_t* slot_mapping, int64_t num_tokens,
+                         void* k_cache, void* v_cache, float* kv_scales, const pkv_desc* desc, void* stream) {
+  if (int e = check_desc(desc, false)) return e;
+  if (desc->kv_dtype != PKV_E4M3) return fail(PKV_ERR_INVALID_ARG, "kv_dtype must be e4m3");
+  if (num_tokens < 0 || num_tokens > 0x7FFFFFFF) return fail(PKV_ERR_INVALID_ARG, "num_tokens out of range");
+  if (desc->num_kv_heads > 65535) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads > 65535");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache || !kv_scales)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  pkv::AppendParams p{};
+  p.k = k;
+  p.v = v;
+  p.slots = slot_mapping;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.kv_scales = kv_scales;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = desc->num_kv_heads;
+  p.head_dim = desc->head_dim;
+  p.num_blocks = desc->num_blocks;
+  return hip_status(pkv::launch_append_e4m3(p, static_cast<hipStream_t>(stream)), "kv_cache_append_e4m3 launch");
+}
+
 int kv_cache_copy_blocks(const int32_t* block_mapping, int32_t num_pairs, void* k_cache, void* v_cache,
                          float* kv_scales, const pkv_desc* desc, void* stream) {
   if (int e = check_desc(desc, false)) return e;

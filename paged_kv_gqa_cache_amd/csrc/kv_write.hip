@@ -9,6 +9,10 @@
 //    "Projects", row 05: E4M3 storage, page scales; "rvLLM: ...", "CUDA
 //    Kernels", row "FP8 KV Cache": per-head scaling).
 //
+//  * append_e4m3_kernel: new tokens quantised into an E4M3 pool one at a
+//    time, growing the block's scale (and re-encoding its earlier codes)
+//    when a token exceeds it, so the scale stays fp32(amax / 448) over the
+//    block's tokens.
 //  * copy_blocks_kernel: whole blocks copied inside the pool, for
 //    copy-on-write forks ("rvLLM: ...", "CUDA Kernels", row "Block Copy":
 //    KV cache block copy for beam search; section "Architecture": the block
@@ -128,6 +132,68 @@ __global__ __launch_bounds__(128) void quantize_e4m3_kernel(const QuantParams p)
   st16(cache + tile + byte, u32x4{w[0], w[1], w[2], w[3]});
   if (tid == 0)
     p.kv_scales[((is_v ? static_cast<size_t>(p.num_blocks) : 0) + blk) * p.num_kv_heads + h] = scale;
+}
+
+// One workgroup (D threads) per (token, kv head, K-or-V); thread d owns dim
+// d of every slot of the block.  Each rounding step is fp32: token scale
+// s = amax / 448; a block's first token sets the scale (1 if s is 0); a
+// later token with s above the stored scale re-encodes the earlier slots as
+// code(clamp(decode(c) * old / s)) and stores s; the token's own code is
+// code(clamp(x / scale)).  At most one token per block per launch.
+__global__ __launch_bounds__(128) void append_e4m3_kernel(const AppendParams p) {
+  const int t = blockIdx.x;
+  const int h = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const int d = threadIdx.x;
+  const int D = p.head_dim;
+  const int64_t slot = p.slots[t];
+  if (slot < 0 || slot >= static_cast<int64_t>(p.num_blocks) * kBlockSize) return;   // whole workgroup
+  const int64_t blk = slot / kBlockSize;
+  const int off = static_cast<int>(slot % kBlockSize);
+  const float x = (is_v ? p.v : p.k)[(static_cast<size_t>(t) * p.num_kv_heads + h) * D + d];
+
+  float amax = fabsf(x);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  __shared__ float sm[2];
+  if ((d & 63) == 0) sm[d >> 6] = amax;
+  __syncthreads();
+  amax = sm[0];
+  if (D > 64) amax = fmaxf(amax, sm[1]);
+  const float s_tok = amax / 448.0f;
+
+  uint8_t* tile = static_cast<uint8_t*>(is_v ? p.v_cache : p.k_cache) +
+                  (static_cast<size_t>(blk) * p.num_kv_heads + h) * kBlockSize * D;
+  auto pos = [&](int tt) -> int {   // byte of (slot tt, dim d) in the tile
+    return is_v ? v_tile_elem(tt, d, 4) : ((d / 16) * kBlockSize + tt) * 16 + d % 16;
+  };
+  float* sc = p.kv_scales + (is_v ? static_cast<size_t>(p.num_blocks) * p.num_kv_heads : 0) +
+              static_cast<size_t>(blk) * p.num_kv_heads + h;
+  float s;
+  if (off == 0) {
+    s = s_tok > 0.f ? s_tok : 1.0f;
+  } else {
+    const float s_old = *sc;
+    s = s_old;
+    if (s_tok > s_old) {
+      for (int o = 0; o < off; ++o) {
+        const uint8_t c = tile[pos(o)];
+        const float v = __builtin_amdgcn_cvt_pk_f32_fp8(c, false)[0] * s_old;
+        tile[pos(o)] = static_cast<uint8_t>(f32_to_e4m3(fminf(fmaxf(v / s_tok, -448.0f), 448.0f)));
+      }
+      s = s_tok;
+    }
+  }
+  tile[pos(off)] = static_cast<uint8_t>(f32_to_e4m3(fminf(fmaxf(x / s, -448.0f), 448.0f)));
+  __syncthreads();   // every thread has read the old scale
+  if (d == 0) *sc = s;
+}
+
+hipError_t launch_append_e4m3(const AppendParams& p, hipStream_t stream) {
+  if (p.num_tokens == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(p.num_tokens), p.num_kv_heads, 2), block(p.head_dim);
+  hipLaunchKernelGGL(append_e4m3_kernel, grid, block, 0, stream, p);
+  return hipGetLastError();
 }
 
 // One thread per 16-byte chunk of a block (a block's Hkv tiles are one

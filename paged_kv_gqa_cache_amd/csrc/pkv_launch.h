@@ -66,6 +66,17 @@ struct QuantParams {
   int32_t num_src_blocks, num_kv_heads, head_dim, num_blocks;
 };
 
+struct AppendParams {
+  const float* k;               // [num_tokens][Hkv][D]
+  const float* v;
+  const int64_t* slots;         // [num_tokens]; negative skips
+  void* k_cache;                // e4m3 pool
+  void* v_cache;
+  float* kv_scales;             // [2][NB][Hkv]
+  int64_t num_tokens;
+  int32_t num_kv_heads, head_dim, num_blocks;
+};
+
 struct CopyParams {
   const int32_t* block_mapping;  // [num_pairs][2]: (src, dst)
   void* k_cache;
@@ -89,5 +100,6 @@ hipError_t launch_stream_merge(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_kv_write(const WriteParams& p, hipStream_t stream);
 hipError_t launch_quantize_e4m3(const QuantParams& p, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
+hipError_t launch_append_e4m3(const AppendParams& p, hipStream_t stream);
 
 }  // namespace pkv

@@ -161,3 +161,12 @@ def test_copy_blocks_validates_before_touching_the_device():
     d8 = desc(kv_dtype=abi.PKV_E4M3)
     assert lib.kv_cache_copy_blocks(FAKE, 2, FAKE, FAKE, None, ctypes.byref(d8), None) == INVALID  # e4m3, no scales
     assert lib.kv_cache_copy_blocks(FAKE, 2, FAKE, FAKE, None, ctypes.byref(desc(kv_dtype=9)), None) == UNSUPPORTED
+
+
+def test_append_e4m3_validates_before_touching_the_device():
+    lib = abi.lib()
+    d8 = desc(kv_dtype=abi.PKV_E4M3)
+    assert lib.kv_cache_append_e4m3(FAKE, FAKE, FAKE, 3, FAKE, FAKE, FAKE, ctypes.byref(desc()), None) == INVALID
+    assert lib.kv_cache_append_e4m3(FAKE, FAKE, FAKE, -1, FAKE, FAKE, FAKE, ctypes.byref(d8), None) == INVALID
+    assert lib.kv_cache_append_e4m3(FAKE, FAKE, FAKE, 3, FAKE, FAKE, None, ctypes.byref(d8), None) == INVALID
+    assert lib.kv_cache_append_e4m3(None, None, None, 0, None, None, None, ctypes.byref(d8), None) == OK

@@ -478,3 +478,74 @@ def test_forked_beam_after_copy_and_write_matches_oracle():
                                      torch.from_numpy(lens).cuda(), w.scale)
     assert max_err(got, want) <= TOL
     assert not np.allclose(want[:B], want[B:])   # the beams did diverge
+
+
+# --------------------------------------------------- E4M3 quantise-on-append ---
+
+def _append_case(seed, mag):
+    """The FP8 pool plus one new token per sequence at position L (scaled by
+    ``mag`` so some (block, head) scales must grow); sequences whose next
+    token would open a block get one from the free list."""
+    w = workloads.generate("qwen25_7b_fp8", num_seqs=5, lengths=("uniform", 1, 300))
+    B, Hkv, D = 5, w.spec.num_kv_heads, w.spec.head_dim
+    L = w.context_lens.astype(np.int64)
+    used = set(int(x) for x in w.block_tables.ravel() if x >= 0)
+    free = [i for i in range(w.num_blocks) if i not in used]
+    tables = np.concatenate([w.block_tables, np.full((B, 1), -1, np.int32)], axis=1)
+    slots = []
+    for b in range(B):
+        j = int(L[b]) // 16
+        if tables[b, j] < 0:
+            tables[b, j] = free.pop(0)
+        slots.append(int(tables[b, j]) * 16 + int(L[b]) % 16)
+    rng = np.random.default_rng(seed)
+    kn = (rng.standard_normal((B, Hkv, D), dtype=np.float32) * np.float32(mag)).astype(np.float32)
+    vn = (rng.standard_normal((B, Hkv, D), dtype=np.float32) * np.float32(mag)).astype(np.float32)
+    return w, tables, np.array(slots, np.int64), kn, vn
+
+
+@pytest.mark.parametrize("seed,mag", [(1, 1.0), (2, 4.0), (3, 0.25)])
+def test_append_e4m3_is_bit_exact(seed, mag):
+    _announce("append e4m3", seed, mag)
+    from paged_kv_gqa_cache_amd import abi
+    w, tables, slots, kn, vn = _append_case(seed, mag)
+    k_o, v_o, s_o = oracle_pool(w)
+    k_g, v_g, s_g = gpu_pool(w)
+    ref.kv_cache_append_e4m3(k_o, v_o, s_o, kn, vn, slots)
+    abi.kv_cache_append_e4m3(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(),
+                             torch.from_numpy(slots).cuda(), k_g, v_g, s_g)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_raw(k_g, "e4m3"), k_o) and np.array_equal(to_raw(v_g, "e4m3"), v_o)
+    assert np.array_equal(s_g.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+    # and attention over the appended tokens agrees with the oracle
+    lens = (w.context_lens + 1).astype(np.int32)
+    want = ref.decode_attention(w.q, "f16", k_o, v_o, "e4m3", tables, lens, w.scale, s_o)
+    got = abi.paged_decode_attention(to_dev(w.q, "f16"), k_g, v_g, torch.from_numpy(tables).cuda(),
+                                     torch.from_numpy(lens).cuda(), w.scale, s_g)
+    assert max_err(got, want) <= TOL
+
+
+def test_append_e4m3_fills_a_block_token_by_token():
+    """Sixteen appends into fresh blocks, magnitudes rising so the scale grows
+    and earlier codes are re-encoded again and again; bit-exact each step."""
+    _announce("append e4m3 fill")
+    from paged_kv_gqa_cache_amd import abi
+    Hkv, D, NB = 4, 128, 8
+    k_o = np.full((NB, Hkv, 16 * D), 0x7F, np.uint8)
+    v_o = k_o.copy()
+    s_o = np.ones((2, NB, Hkv), np.float32)
+    k_g, v_g = torch.from_numpy(k_o.copy()).cuda(), torch.from_numpy(v_o.copy()).cuda()
+    s_g = torch.from_numpy(s_o.copy()).cuda()
+    rng = np.random.default_rng(7)
+    blocks = np.array([5, 2, 7], np.int64)
+    for t in range(16):
+        growth = np.float32(1.0 + 0.4 * t)
+        kn = (rng.standard_normal((3, Hkv, D), dtype=np.float32) * growth).astype(np.float32)
+        vn = (rng.standard_normal((3, Hkv, D), dtype=np.float32) * growth).astype(np.float32)
+        slots = blocks * 16 + t
+        ref.kv_cache_append_e4m3(k_o, v_o, s_o, kn, vn, slots)
+        abi.kv_cache_append_e4m3(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(),
+                                 torch.from_numpy(slots).cuda(), k_g, v_g, s_g)
+        torch.cuda.synchronize()
+        assert np.array_equal(k_g.cpu().numpy(), k_o) and np.array_equal(v_g.cpu().numpy(), v_o), t
+        assert np.array_equal(s_g.cpu().numpy().view(np.uint32), s_o.view(np.uint32)), t
