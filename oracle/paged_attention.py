@@ -271,6 +271,36 @@ def partition_origin(context_len: int, window: int) -> int:
     return window_start(context_len, window) // BLOCK_SIZE * BLOCK_SIZE
 
 
+def prefill_attention(q_raw, q_dtype: str, k_cache, v_cache, kv_dtype: str, block_tables,
+                      context_lens, query_start, scale: float, kv_scales=None):
+    """Multi-token step: float64 [T, Hq, D] for the packed query rows.
+
+    Sequence b owns query rows query_start[b] .. query_start[b+1]-1: its
+    n_b newest tokens, at positions L_b - n_b .. L_b - 1.  Row j (position
+    p = L_b - n_b + j) attends to positions 0 .. p: causal inside the new
+    tokens ("rvLLM: High-performance LLM inference in Rust", section "CUDA
+    Kernels", row "FlashAttention-2": prefill and decode with causal
+    masking).  With n_b = 1 this is decode_attention.
+    """
+    q = to_f64(q_raw, q_dtype)
+    T, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    qs = np.asarray(query_start, dtype=np.int64)
+    for b in range(len(qs) - 1):
+        L = int(context_lens[b])
+        n = int(qs[b + 1] - qs[b])
+        for h in range(Hkv):
+            K, V = gather(k_cache, v_cache, kv_dtype, block_tables[b], L, h, D, kv_scales)
+            for j in range(n):
+                p = L - n + j
+                for g in range(G):
+                    i = h * G + g
+                    out[qs[b] + j, i] = softmax_weights(q[qs[b] + j, i], K[:p + 1], scale) @ V[:p + 1]
+    return out
+
+
 def num_partitions(context_len: int, partition_size: int, window: int = 0) -> int:
     a = partition_origin(context_len, window)
     return (int(context_len) - a + partition_size - 1) // partition_size

@@ -24,6 +24,8 @@ qwen25_7b_prefix   128   28/4     128  bf16    lognormal(median 1024, sigma 1)  
                                                clipped to [16, 32768]            32 prefix blocks
 qwen25_7b_fp8      64    28/4     128  e4m3    fixed 8192                        q f16
 gemma_sliding      64    32/16    128  bf16    uniform [1024, 32768]             window 1024
+qwen25_7b_chunk    16    28/4     128  bf16    uniform [512, 4096]               1-256 new
+                                                                                 tokens each
 =================  ====  =======  ===  ======  ================================  ============
 
 Recipe (one ``numpy.random.default_rng(seed)`` per workload, draws in this
@@ -34,6 +36,10 @@ new token's K then V [B, Hkv, D] where the workload writes one.  Values are
 float32 N(0, 1) rounded to nearest-even into f16/bf16.  Slots no sequence
 owns stay unwritten (the caller fills the pool with NaN first).  The pool
 holds ceil(1.25 x blocks needed) blocks unless the workload fixes it.
+A multi-token workload (chunked prefill, speculative verification) gives
+each sequence n_b query tokens, the last n_b positions of its context
+(n_b drawn uniformly, at most L_b); q is then [sum n_b, Hq, D] with rows in
+sequence order and query_start [B + 1] the offsets.
 With a window of W tokens only the blocks holding positions
 [max(0, L - W), L) get their own ids and values; every table entry before
 them points at one shared block that is never written (it keeps the
@@ -72,6 +78,7 @@ class WorkloadSpec:
     new_token_write: bool = False  # the step starts with kv_cache_write of one token per sequence
     partition_size: int = 512      # default split-context partition (tokens)
     window: int = 0                # sliding window in tokens (0: whole context)
+    query_tokens: tuple = ()       # multi-token step: ("uniform", lo, hi) new tokens per sequence
 
     @property
     def group_size(self) -> int:
@@ -92,6 +99,9 @@ SPECS = {
                                   ("fixed", 8192), partition_size=1024),
     "gemma_sliding": WorkloadSpec("gemma_sliding", 1006, 64, 32, 16, 128, "bf16", "bf16",
                                   ("uniform", 1024, 32768), partition_size=512, window=1024),
+    "qwen25_7b_chunk": WorkloadSpec("qwen25_7b_chunk", 1007, 16, 28, 4, 128, "bf16", "bf16",
+                                    ("uniform", 512, 4096), partition_size=512,
+                                    query_tokens=("uniform", 1, 256)),
 }
 
 
@@ -111,6 +121,7 @@ class Workload:
     new_slots: Optional[np.ndarray] = None   # int64 [B] slot of each sequence's new token
     new_k: Optional[np.ndarray] = None       # raw [B, Hkv, D] in kv_dtype
     new_v: Optional[np.ndarray] = None
+    query_start: Optional[np.ndarray] = None # int32 [B + 1] (multi-token workloads)
     meta: dict = field(default_factory=dict)
 
     # -- views used by both consumers (data plumbing only) -----------------
@@ -226,7 +237,16 @@ def generate(name: str, **overrides) -> Workload:
     fill_blocks = np.array(fill_blocks, dtype=np.int64)
     fill_valid = np.array(fill_valid, dtype=np.int32)
 
-    q = round_to(rng.standard_normal((B, Hq, D), dtype=np.float32), spec.q_dtype)
+    query_start = None
+    if spec.query_tokens:
+        if spec.new_token_write or W:
+            raise ValueError("a multi-token workload has no new-token write and no window")
+        lo_q, hi_q = spec.query_tokens[1], spec.query_tokens[2]
+        nq = np.minimum(rng.integers(lo_q, hi_q, size=B, endpoint=True), L).astype(np.int64)
+        query_start = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+        q = round_to(rng.standard_normal((int(query_start[-1]), Hq, D), dtype=np.float32), spec.q_dtype)
+    else:
+        q = round_to(rng.standard_normal((B, Hq, D), dtype=np.float32), spec.q_dtype)
     ctx_dtype = "f32" if spec.kv_dtype == "e4m3" else spec.kv_dtype
     n = len(fill_blocks)
     kf = rng.standard_normal((n, BLOCK_SIZE, Hkv, D), dtype=np.float32)
@@ -250,7 +270,8 @@ def generate(name: str, **overrides) -> Workload:
     scale = float(np.float32(1.0 / math.sqrt(D)))
     meta = {"blocks_needed": needed, "outside_block": outside_id}
     return Workload(spec, num_blocks, scale, q, L.astype(np.int32), tables, fill_blocks,
-                    fill_valid, fill_k, fill_v, ctx_dtype, new_slots, new_k, new_v, meta)
+                    fill_valid, fill_k, fill_v, ctx_dtype, new_slots, new_k, new_v,
+                    query_start=query_start, meta=meta)
 
 
 def kv_bytes(w: Workload, unique: bool = True) -> int:

@@ -599,3 +599,72 @@ def test_pool_append_matches_per_head_steps_and_leaves_other_slots():
     touched = set(int(s // 16) for s in slots if s >= 0)
     others = [i for i in range(w.num_blocks) if i not in touched]
     assert np.array_equal(k[others], k0[others]) and np.array_equal(sc[:, others], s0[:, others])
+
+
+# ------------------------------------------------- multi-token (causal) step ---
+
+def _chunk(**kw):
+    base = dict(num_seqs=3, lengths=("uniform", 1, 70), query_tokens=("uniform", 1, 20), head_dim=64,
+                num_q_heads=8, num_kv_heads=2)
+    base.update(kw)
+    return small("qwen25_7b_chunk", **base)
+
+
+def _prefill(w, pool=None):
+    k, v, sc = pool if pool is not None else oracle_pool(w)
+    return ref.prefill_attention(w.q, w.spec.q_dtype, k, v, w.spec.kv_dtype, w.block_tables,
+                                 w.context_lens, w.query_start, w.scale, sc)
+
+
+def test_prefill_oracle_matches_python_triple_loop():
+    w = _chunk()
+    out = _prefill(w)
+    q = ref.to_f64(w.q, "bf16")
+    G = w.spec.group_size
+    for b in range(w.spec.num_seqs):
+        L, q0, q1 = int(w.context_lens[b]), int(w.query_start[b]), int(w.query_start[b + 1])
+        for h in range(w.spec.num_kv_heads):
+            K, V = logical_kv(w, b, h)
+            for j in range(q1 - q0):
+                p = L - (q1 - q0) + j
+                for g in range(G):
+                    bf = bruteforce.attention_one_query(q[q0 + j, h * G + g].tolist(), K[:p + 1].tolist(),
+                                                        V[:p + 1].tolist(), w.scale)
+                    np.testing.assert_allclose(out[q0 + j, h * G + g], bf, rtol=0, atol=1e-12)
+
+
+def test_prefill_oracle_matches_torch_sdpa_with_a_causal_mask():
+    w = _chunk(num_seqs=4, lengths=("uniform", 40, 300), query_tokens=("uniform", 1, 64), head_dim=128)
+    out = _prefill(w)
+    q = torch.from_numpy(ref.to_f64(w.q, "bf16"))
+    G = w.spec.group_size
+    for b in range(4):
+        L, q0, q1 = int(w.context_lens[b]), int(w.query_start[b]), int(w.query_start[b + 1])
+        n = q1 - q0
+        mask = torch.from_numpy(np.arange(L)[None, :] <= (L - n + np.arange(n))[:, None])   # [n, L]
+        for h in range(w.spec.num_kv_heads):
+            K, V = logical_kv(w, b, h)
+            o = torch.nn.functional.scaled_dot_product_attention(
+                q[q0:q1, h * G:(h + 1) * G].transpose(0, 1), torch.from_numpy(K)[None].expand(G, -1, -1),
+                torch.from_numpy(V)[None].expand(G, -1, -1), attn_mask=mask, scale=w.scale)   # [G, n, D]
+            np.testing.assert_allclose(out[q0:q1, h * G:(h + 1) * G], o.transpose(0, 1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_prefill_rows_equal_decode_at_their_own_position():
+    """Row j of sequence b equals one-query decode over the first p_j + 1
+    positions; with one new token per sequence the step is decode itself."""
+    w = _chunk(num_seqs=3, lengths=("uniform", 20, 200), query_tokens=("uniform", 1, 30))
+    k, v, _ = oracle_pool(w)
+    out = _prefill(w, (k, v, None))
+    for b in range(3):
+        L, q0, q1 = int(w.context_lens[b]), int(w.query_start[b]), int(w.query_start[b + 1])
+        for j in range(q1 - q0):
+            p = L - (q1 - q0) + j
+            one = ref.decode_attention(w.q[q0 + j:q0 + j + 1], "bf16", k, v, "bf16", w.block_tables[b:b + 1],
+                                       np.array([p + 1], np.int32), w.scale)
+            assert np.array_equal(out[q0 + j], one[0])
+    w1 = _chunk(num_seqs=4, query_tokens=("uniform", 1, 1))
+    k1, v1, _ = oracle_pool(w1)
+    assert np.array_equal(_prefill(w1, (k1, v1, None)),
+                          ref.decode_attention(w1.q, "bf16", k1, v1, "bf16", w1.block_tables, w1.context_lens,
+                                               w1.scale))
