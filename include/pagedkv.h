@@ -315,6 +315,44 @@ int paged_decode_attention_balanced(const void* q, const void* k_cache, const vo
  * device (it grows with the number of waves the device holds), or -1.  */
 int64_t paged_decode_balanced_workspace_bytes(const pkv_desc* desc);
 
+/*
+ * paged_prefill_attention - attention for several new tokens per sequence
+ * (chunked prefill, speculative verification), causal inside the new
+ * tokens ("rvLLM: High-performance LLM inference in Rust", section "CUDA
+ * Kernels", row "FlashAttention-2": prefill and decode with causal
+ * masking; row "PagedAttention V2": the block-table gather).
+ *
+ *   q             [num_query_tokens][Hq][D] in q_dtype: the query rows of all
+ *                 sequences, sequence-major
+ *   query_start   int32 [B + 1]: sequence b owns rows query_start[b] ..
+ *                 query_start[b+1] - 1 (0 = query_start[0] <= ... <=
+ *                 query_start[B] = num_query_tokens), its n_b newest tokens,
+ *                 at positions L_b - n_b .. L_b - 1 of its context (n_b <=
+ *                 L_b; their K/V are already in the cache)
+ *   context_lens  int32 [B]: L_b, including the new tokens
+ *   partition_size  0: one pass per (sequence, kv head, pack of tokens);
+ *                 else a positive multiple of 16: split the keys into
+ *                 partitions of that many positions and merge their
+ *                 log-sum-exp partials (needs the workspace)
+ *   workspace     device memory of workspace_bytes >=
+ *                 paged_prefill_workspace_bytes(desc, num_query_tokens,
+ *                 partition_size) bytes, 256-byte aligned (NULL when
+ *                 partition_size is 0)
+ *   out           [num_query_tokens][Hq][D] in out_dtype
+ * The row of token j of sequence b (position p = L_b - n_b + j) attends to
+ * positions 0 .. p.  Other arguments as paged_decode_attention.  Requires
+ * num_seqs <= 2048 and sliding_window = 0 (else PKV_ERR_UNSUPPORTED).
+ */
+int paged_prefill_attention(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const int32_t* query_start, int32_t num_query_tokens, float scale,
+                            const float* kv_scales, int32_t partition_size, void* workspace,
+                            int64_t workspace_bytes, void* out, const pkv_desc* desc, void* stream);
+
+/* Workspace bytes paged_prefill_attention needs (0 for partition_size 0), or -1.  */
+int64_t paged_prefill_workspace_bytes(const pkv_desc* desc, int32_t num_query_tokens,
+                                      int32_t partition_size);
+
 /* S = ceil(MBPS * 16 / partition_size), or -1 on invalid arguments.  */
 int64_t paged_decode_num_partitions(const pkv_desc* desc, int32_t partition_size);
 

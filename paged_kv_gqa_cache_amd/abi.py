@@ -60,6 +60,8 @@ def _load():
         "paged_decode_split_workspace_bytes": (ctypes.c_int64, [D, I32]),
         "paged_decode_attention_balanced": (ctypes.c_int, [P, P, P, P, P, F, P, P, I64, P, D, P]),
         "paged_decode_balanced_workspace_bytes": (ctypes.c_int64, [D]),
+        "paged_prefill_attention": (ctypes.c_int, [P, P, P, P, P, P, I32, F, P, I32, P, I64, P, D, P]),
+        "paged_prefill_workspace_bytes": (ctypes.c_int64, [D, I32, I32]),
         "paged_decode_num_partitions": (ctypes.c_int64, [D, I32]),
         "paged_decode_workspace_bytes": (ctypes.c_int64, [D, I32]),
         "pkv_last_error": (ctypes.c_char_p, []),
@@ -77,6 +79,7 @@ EXPORTED = ("kv_cache_write", "kv_cache_quantize_e4m3", "kv_cache_append_e4m3", 
             "paged_decode_attention_partial", "paged_decode_attention_reduce",
             "paged_decode_attention_split", "paged_decode_split_workspace_bytes",
             "paged_decode_attention_balanced", "paged_decode_balanced_workspace_bytes",
+            "paged_prefill_attention", "paged_prefill_workspace_bytes",
             "paged_decode_num_partitions", "paged_decode_workspace_bytes", "pkv_last_error",
             "pkv_version")
 
@@ -261,4 +264,32 @@ def paged_decode_attention_balanced(q, k_cache, v_cache, block_tables, context_l
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         float(scale), _ptr(kv_scales), _ptr(workspace), workspace.numel(),
         _ptr(out), ctypes.byref(desc), _stream(stream)))
+    return out
+
+
+def prefill_workspace(q, k_cache, block_tables, partition_size: int):
+    """A workspace for paged_prefill_attention (None for partition_size 0)."""
+    if partition_size == 0:
+        return None
+    desc = make_desc(block_tables.shape[0], q.shape[1], k_cache.shape[1], q.shape[2], k_cache.shape[0],
+                     block_tables.shape[1], _code(q), _code(k_cache), PKV_F32)
+    n = _lib.paged_prefill_workspace_bytes(ctypes.byref(desc), int(q.shape[0]), int(partition_size))
+    if n < 0:
+        raise PkvError("paged_prefill_workspace_bytes", 1, last_error())
+    return torch.empty(int(n), dtype=torch.uint8, device=q.device)
+
+
+def paged_prefill_attention(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, kv_scales=None,
+                            partition_size=0, workspace=None, out=None, out_dtype=None, stream=None):
+    """Causal attention for query rows q [T, Hq, D] packed by query_start [B + 1]."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    if partition_size and workspace is None:
+        workspace = prefill_workspace(q, k_cache, block_tables, partition_size)
+    desc = make_desc(block_tables.shape[0], q.shape[1], k_cache.shape[1], q.shape[2], k_cache.shape[0],
+                     block_tables.shape[1], _code(q), _code(k_cache), _code(out))
+    _check("paged_prefill_attention", _lib.paged_prefill_attention(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), _ptr(query_start),
+        int(q.shape[0]), float(scale), _ptr(kv_scales), int(partition_size), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _ptr(out), ctypes.byref(desc), _stream(stream)))
     return out

@@ -402,6 +402,76 @@ int paged_decode_attention_balanced(const void* q, const void* k_cache, const vo
   return hip_status(pkv::launch_stream_merge(r, st), "paged_decode_attention_balanced merge launch");
 }
 
+int64_t paged_prefill_workspace_bytes(const pkv_desc* desc, int32_t num_query_tokens, int32_t partition_size) {
+  if (check_desc(desc, false)) return -1;
+  if (num_query_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_query_tokens < 0"), -1;
+  if (partition_size == 0) return 0;
+  if (check_partition(partition_size)) return -1;
+  const int64_t rows = static_cast<int64_t>(num_query_tokens) * desc->num_q_heads * partitions(desc, partition_size);
+  return align256(rows * 4) + rows * desc->head_dim * 4;
+}
+
+int paged_prefill_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* query_start, int32_t num_query_tokens,
+                            float scale, const float* kv_scales, int32_t partition_size, void* workspace,
+                            int64_t workspace_bytes, void* out, const pkv_desc* desc, void* stream) {
+  if (int e = check_desc(desc, true)) return e;
+  if (int e = check_attn_types(desc, kv_scales)) return e;
+  if (desc->num_seqs > 2048)
+    return fail(PKV_ERR_UNSUPPORTED, "multi-token step takes at most 2048 sequences (got %d)", desc->num_seqs);
+  if (desc->sliding_window != 0) return fail(PKV_ERR_UNSUPPORTED, "multi-token step has no sliding window");
+  if (partition_size != 0)
+    if (int e = check_partition(partition_size)) return e;
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  if (num_query_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_query_tokens < 0");
+  if (static_cast<int64_t>(num_query_tokens) * desc->num_q_heads > 0x7FFFFFFF / 2)
+    return fail(PKV_ERR_INVALID_ARG, "num_query_tokens * num_q_heads too large");
+  if (desc->num_seqs == 0 || num_query_tokens == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  pkv::DecodeParams p = decode_params(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales, desc);
+  p.query_start = query_start;
+  p.num_query_tokens = num_query_tokens;
+  p.tokens_per_pack = 16 / p.group;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (partition_size == 0) {
+    p.out = out;
+    p.partition_blocks = desc->max_blocks_per_seq;
+    p.num_partitions = 1;
+    return hip_status(pkv::launch_prefill(p, desc->kv_dtype, desc->head_dim, 0, st), "paged_prefill_attention launch");
+  }
+  const int64_t s_parts = partitions(desc, partition_size);
+  const int64_t rows = static_cast<int64_t>(num_query_tokens) * desc->num_q_heads * s_parts;
+  const int64_t need = align256(rows * 4) + rows * desc->head_dim * 4;
+  if (!workspace) return fail(PKV_ERR_INVALID_ARG, "null workspace");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(PKV_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_INVALID_ARG, "workspace of %lld bytes is smaller than the %lld needed",
+                static_cast<long long>(workspace_bytes), static_cast<long long>(need));
+  char* ws = static_cast<char*>(workspace);
+  p.tmp_lse = reinterpret_cast<float*>(ws);
+  p.tmp_out = reinterpret_cast<float*>(ws + align256(rows * 4));
+  p.partition_blocks = partition_size / 16;
+  p.num_partitions = static_cast<int32_t>(s_parts);
+  if (int e = hip_status(pkv::launch_prefill(p, desc->kv_dtype, desc->head_dim, 1, st), "paged_prefill_attention launch"))
+    return e;
+  pkv::ReduceParams r{};
+  r.tmp_out = p.tmp_out;
+  r.tmp_lse = p.tmp_lse;
+  r.context_lens = context_lens;
+  r.out = out;
+  r.num_seqs = desc->num_seqs;
+  r.num_q_heads = desc->num_q_heads;
+  r.head_dim = desc->head_dim;
+  r.mbps = desc->max_blocks_per_seq;
+  r.partition_size = partition_size;
+  r.num_partitions = p.num_partitions;
+  r.out_dtype = desc->out_dtype;
+  r.query_start = query_start;
+  r.num_query_tokens = num_query_tokens;
+  return hip_status(pkv::launch_prefill_merge(r, st), "paged_prefill_attention merge launch");
+}
+
 int paged_decode_attention_reduce(const float* tmp_out, const float* tmp_lse,
                                   const int32_t* context_lens, int32_t partition_size, void* out,
                                   const pkv_desc* desc, void* stream) {

@@ -359,8 +359,8 @@ struct WaveState {
   float m;
   float l;
   f32x4 o[NT];
-  __device__ void reset() {
-    m = -INFINITY;
+  __device__ void reset(float m0 = -INFINITY) {
+    m = m0;
     l = 0.f;
 #pragma unroll
     for (int n = 0; n < NT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -368,14 +368,15 @@ struct WaveState {
 };
 
 // Streams the blocks first + stride*i (i < count) of sequence b (context
-// length L, kv head h, positions before lo masked off) through one wave's
-// softmax state.  `ids` holds the
+// length L, kv head h, positions before lo masked off; with CAUSAL, each
+// lane's head column also masks positions after its own limit lim) through
+// one wave's softmax state.  `ids` holds the
 // physical ids of the first 64 of them (lane j: block first + stride*j).
-template <int KVT, int D, int PF>
+template <int KVT, int D, int PF, bool CAUSAL = false>
 __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int h, int L, int lo, int first,
                                               int stride, int count, int ids,
                                               const u32x4 (&qop)[TileOps<KVT, D>::NQ],
-                                              WaveState<D / 16>& st) {
+                                              WaveState<D / 16>& st, int lim = 0) {
   typedef TileOps<KVT, D> T;
   constexpr int E = ElemBytes<KVT>::value;
   constexpr int TILE = kBlockSize * D * E;  // bytes of one (block, kv head) tile
@@ -439,6 +440,11 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int 
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[j] = (j < nlo) ? -INFINITY : x[j];
     }
+    if constexpr (CAUSAL) {       // this lane's column sees positions <= lim only
+      const int nc = lim - tok0 - 4 * g;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = (j <= nc) ? x[j] : -INFINITY;
+    }
     // Lazy rescaling: the reference max only moves when some head's block
     // max exceeds it by more than kSlack (log2 units), so exp2(x - m) stays
     // below 2^kSlack and the accumulators are rescaled about once per run
@@ -487,6 +493,49 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int 
   if constexpr (KVT == KV_E4M3) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) st.o[n] *= T::kOutScale;
+  }
+}
+
+// Merges the NW waves' softmax states of one item through LDS: M and Lsum
+// get the combined max and sum of this lane's head column, and emit(n, acc)
+// receives the normalised output d-tiles n = wid, wid + NW, ...
+template <int NW, int NT, typename Emit>
+__device__ __forceinline__ void merge_waves(float m_run, float l_run, const f32x4 (&o)[NT],
+                                            ItemShared<NW, NT>& sm, int wid, int lane, float& M,
+                                            float& Lsum, Emit emit) {
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  if constexpr (NW > 1) {
+    if (g == 0) {
+      sm.m[wid][r] = m_run;
+      sm.l[wid][r] = l_run;
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) sm.o[wid][n][lane] = o[n];
+    __syncthreads();
+    float fw[NW];
+    M = sm.m[0][r];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm.m[w][r]);
+    Lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      fw[w] = fast_exp2(sm.m[w][r] - M);
+      Lsum += fw[w] * sm.l[w][r];
+    }
+    const float inv = 1.f / Lsum;
+    for (int n = wid; n < NT; n += NW) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc += fw[w] * sm.o[w][n][lane];
+      emit(n, acc * inv);
+    }
+  } else {
+    M = m_run;
+    Lsum = l_run;
+    const float inv = 1.f / Lsum;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) emit(n, o[n] * inv);
   }
 }
 
@@ -546,38 +595,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
     }
   };
   float M, Lsum;
-  if constexpr (NW > 1) {
-    if (g == 0) {
-      sm.m[wid][r] = m_run;
-      sm.l[wid][r] = l_run;
-    }
-#pragma unroll
-    for (int n = 0; n < NT; ++n) sm.o[wid][n][lane] = o[n];
-    __syncthreads();
-    float fw[NW];
-    M = sm.m[0][r];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm.m[w][r]);
-    Lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      fw[w] = fast_exp2(sm.m[w][r] - M);
-      Lsum += fw[w] * sm.l[w][r];
-    }
-    const float inv = 1.f / Lsum;
-    for (int n = wid; n < NT; n += NW) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < NW; ++w) acc += fw[w] * sm.o[w][n][lane];
-      emit(n, acc * inv);
-    }
-  } else {
-    M = m_run;
-    Lsum = l_run;
-    const float inv = 1.f / Lsum;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) emit(n, o[n] * inv);
-  }
+  merge_waves<NW, NT>(m_run, l_run, o, sm, wid, lane, M, Lsum, emit);
   if (direct) return;
   const float lse = (M + fast_log2(Lsum)) * kLn2;
   if constexpr (MODE == MODE_SPLIT) {
@@ -720,6 +738,213 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_persistent(const DecodeP
     part = part2;
     cur = nxt;
   }
+}
+
+// ------------------------------------------------------ multi-token step
+// Several new tokens per sequence (chunked prefill, speculative
+// verification): sequence b's query rows query_start[b] .. query_start[b+1]-1
+// are its n_b newest tokens, at positions L - n_b .. L - 1, and the row of
+// token j attends causally to positions 0 .. L - n_b + j ("rvLLM:
+// High-performance LLM inference in Rust", section "CUDA Kernels", row
+// "FlashAttention-2": prefill and decode with causal masking).  A pack of
+// TP = 16 / G tokens x G heads fills the 16 matrix-core columns, so each K/V
+// tile fetched serves TP tokens of the whole group, and each column masks the
+// positions after its own token.  Work items are (sequence, kv head, pack,
+// partition); a pack's partitions cover the blocks up to its last token.
+struct QueryRows {
+  int q0;   // first query row of the sequence
+  int n;    // its number of query rows (<= its context length)
+};
+
+template <int KVT, int D, int NW>
+__device__ __forceinline__ void prefill_prefetch(const DecodeParams& p, int b, int h, int pack, int part,
+                                                 QueryRows qrow, ItemPrefetch<KVT, D>& pf) {
+  constexpr int QB = (KVT == KV_F32) ? 4 : 2;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15;
+  const int G = p.group;
+  const int j0 = pack * p.tokens_per_pack;
+  const int ncols = min(p.tokens_per_pack, qrow.n - j0) * G;
+  const auto tr = make_tile_rsrc(p.block_tables + static_cast<size_t>(b) * p.mbps, p.mbps * 4);
+  const int id0 = part * p.partition_blocks + wid + NW * lane;
+  pf.ids = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(tr, static_cast<uint32_t>(id0) * 4u, 0, 0));
+  const uint32_t row_bytes = static_cast<uint32_t>(p.num_q_heads * D * QB);
+  const auto qr = make_tile_rsrc(static_cast<const char*>(p.q) + static_cast<size_t>(qrow.q0) * row_bytes,
+                                 qrow.n * row_bytes);
+  // Column r: token j0 + r / G, head h * G + r % G; unused columns read
+  // past the descriptor's end, i.e. zeros.
+  const uint32_t qoff = r < ncols ? static_cast<uint32_t>(((j0 + r / G) * p.num_q_heads + h * G + r % G) * D * QB)
+                                  : static_cast<uint32_t>(qrow.n) * row_bytes;
+  TileOps<KVT, D>::load_q(pf.qop, qr, qoff, lane >> 4);
+}
+
+template <int KVT, int D, int NW, int MODE, int PF>
+__device__ __forceinline__ void prefill_item(const DecodeParams& p, int b, int h, int pack, int part, int L,
+                                             QueryRows qrow, const ItemPrefetch<KVT, D>& pf,
+                                             ItemShared<NW, D / 16>& sm) {
+  constexpr int NT = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  const int G = p.group;
+  const int j0 = pack * p.tokens_per_pack;
+  const int ntok = min(p.tokens_per_pack, qrow.n - j0);
+  const bool valid = r < ntok * G;
+  const int jj = valid ? r / G : ntok - 1;
+  const int pos = L - qrow.n + j0 + jj;             // last position this column sees
+  const int l_item = L - qrow.n + j0 + ntok;        // positions the pack reads
+  const int nblk = (l_item + kBlockSize - 1) / kBlockSize;
+  const int blk0 = part * p.partition_blocks;
+  if (blk0 >= nblk) return;
+  const int blk1 = min(nblk, blk0 + p.partition_blocks);
+  const int first = blk0 + wid;
+  const int nmine = first < blk1 ? (blk1 - first + NW - 1) / NW : 0;
+  WaveState<NT> st;
+  st.reset(-1e30f);   // finite: a column may see no position in a wave's blocks
+  attend_blocks<KVT, D, PF, true>(p, b, h, l_item, 0, first, NW, nmine, pf.ids, pf.qop, st, pos);
+  const float l_run = sum_over_groups(st.l);
+
+  const size_t row = static_cast<size_t>(qrow.q0 + j0 + jj) * p.num_q_heads + h * G + r % G;
+  const bool col_ok = valid && blk0 * kBlockSize <= pos;   // the partition holds a position of the column
+  auto emit = [&](int n, f32x4 acc) {
+    if (!col_ok) return;
+    if (MODE == MODE_FINAL) store4(p.out, row * D + 16 * n + 4 * g, p.out_dtype, acc);
+    else *reinterpret_cast<f32x4*>(p.tmp_out + (row * p.num_partitions + part) * D + 16 * n + 4 * g) = acc;
+  };
+  float M, Lsum;
+  merge_waves<NW, NT>(st.m, l_run, st.o, sm, wid, lane, M, Lsum, emit);
+  if (MODE == MODE_PARTIAL && wid == 0 && g == 0 && col_ok)
+    p.tmp_lse[row * p.num_partitions + part] = (M + fast_log2(Lsum)) * kLn2;
+}
+
+// Persistent form of the multi-token step, laid out like
+// paged_decode_persistent: LDS prefix sums of each sequence's items, XCD
+// ranges, the next item's ids and q prefetched during the current one.
+template <int KVT, int D, int NW, int MODE, int PF>
+__global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const DecodeParams p) {
+  __shared__ ItemShared<NW, D / 16> sm;
+  __shared__ int s_cum[kMaxSeqsPersistent + 1];   // items before sequence b
+  __shared__ int s_len[kMaxSeqsPersistent];       // context length
+  __shared__ int s_q0[kMaxSeqsPersistent];        // first query row
+  __shared__ int s_nq[kMaxSeqsPersistent];        // query rows
+  __shared__ int s_wsum[NW];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int B = p.num_seqs;
+  const int Hkv = p.num_kv_heads;
+  const int TP = p.tokens_per_pack;
+  auto parts_of = [&](int L, int n) {   // partitions of each pack of a sequence
+    return n > 0 ? ((L + kBlockSize - 1) / kBlockSize + p.partition_blocks - 1) / p.partition_blocks : 0;
+  };
+
+  int carry = 0;
+  for (int c0 = 0; c0 < B; c0 += NW * 64) {
+    const int i = c0 + static_cast<int>(threadIdx.x);
+    int items = 0;
+    if (i < B) {
+      const int L = max(0, min(p.context_lens[i], p.mbps * kBlockSize));
+      const int q0 = max(0, min(p.query_start[i], p.num_query_tokens));
+      const int q1 = max(q0, min(p.query_start[i + 1], p.num_query_tokens));
+      const int n = min(q1 - q0, L);
+      s_len[i] = L;
+      s_q0[i] = q0;
+      s_nq[i] = n;
+      items = Hkv * ((n + TP - 1) / TP) * parts_of(L, n);
+    }
+    int x = items;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wsum[wid] = x;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wid; ++w) before += s_wsum[w];
+    int total = 0;
+    for (int w = 0; w < NW; ++w) total += s_wsum[w];
+    if (i < B) s_cum[i + 1] = before + x;
+    if (i == 0) s_cum[0] = 0;
+    carry += total;
+    __syncthreads();
+  }
+  const int N = carry;
+  const int xcd = blockIdx.x % kXcds;
+  const int per_xcd = gridDim.x / kXcds;
+  const int lo = static_cast<int>(static_cast<int64_t>(N) * xcd / kXcds);
+  const int hi = static_cast<int>(static_cast<int64_t>(N) * (xcd + 1) / kXcds);
+  // Item n -> (sequence, kv head, pack, partition), partition fastest.
+  auto locate = [&](int n, int& b, int& h, int& pack, int& part) {
+    int lo_b = 0, hi_b = B;
+    while (hi_b - lo_b > 1) {
+      const int mid = (lo_b + hi_b) >> 1;
+      if (s_cum[mid] <= n) lo_b = mid;
+      else hi_b = mid;
+    }
+    b = lo_b;
+    const int parts = parts_of(s_len[b], s_nq[b]);
+    const int per_head = ((s_nq[b] + TP - 1) / TP) * parts;
+    const int local = n - s_cum[b];
+    h = local / per_head;
+    const int rem = local % per_head;
+    pack = rem / parts;
+    part = rem % parts;
+  };
+  int n = lo + static_cast<int>(blockIdx.x) / kXcds;
+  if (n >= hi) return;
+  int b, h, pack, part, b2, h2, pack2, part2;
+  ItemPrefetch<KVT, D> cur, nxt;
+  locate(n, b, h, pack, part);
+  prefill_prefetch<KVT, D, NW>(p, b, h, pack, part, QueryRows{s_q0[b], s_nq[b]}, cur);
+  while (true) {
+    const int n2 = n + per_xcd;
+    locate(min(n2, hi - 1), b2, h2, pack2, part2);
+    prefill_prefetch<KVT, D, NW>(p, b2, h2, pack2, part2, QueryRows{s_q0[b2], s_nq[b2]}, nxt);
+    prefill_item<KVT, D, NW, MODE, PF>(p, b, h, pack, part, s_len[b], QueryRows{s_q0[b], s_nq[b]}, cur, sm);
+    __syncthreads();   // the next item reuses the merge state
+    if (n2 >= hi) break;
+    n = n2;
+    b = b2;
+    h = h2;
+    pack = pack2;
+    part = part2;
+    cur = nxt;
+  }
+}
+
+// One wave per (query row, head): merges the row's partitions 0 ..
+// ceil((position + 1) / P) - 1.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(const ReduceParams p) {
+  const int lane = threadIdx.x & 63;
+  const int pair = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));  // wave-uniform
+  if (pair >= p.num_query_tokens * p.num_q_heads) return;
+  const int t = pair / p.num_q_heads;
+  // Sequence of row t: last b with query_start[b] <= t.
+  int lo_b = 0, hi_b = p.num_seqs;
+  while (hi_b - lo_b > 1) {
+    const int mid = (lo_b + hi_b) >> 1;
+    if (p.query_start[mid] <= t) lo_b = mid;
+    else hi_b = mid;
+  }
+  const int b = lo_b;
+  const int L = max(0, min(p.context_lens[b], p.mbps * kBlockSize));
+  const int q0 = max(0, min(p.query_start[b], p.num_query_tokens));
+  const int q1 = max(q0, min(p.query_start[b + 1], p.num_query_tokens));
+  const int nq = min(q1 - q0, L);
+  float acc[D / 64];
+  if (t - q0 >= nq || t < q0) {   // no such row in a consistent batch: zeros
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) acc[k] = 0.f;
+  } else {
+    const int pos = L - nq + (t - q0);
+    const int n = min((pos + p.partition_size) / p.partition_size, p.num_partitions);
+    merge_partitions<D, false>(p.tmp_lse + static_cast<size_t>(pair) * p.num_partitions,
+                               p.tmp_out + static_cast<size_t>(pair) * p.num_partitions * D, n, lane, acc);
+  }
+  store_row_part<D>(p.out, pair, lane, p.out_dtype, acc);
 }
 
 // ------------------------------------------------------ balanced schedule
@@ -1046,6 +1271,41 @@ hipError_t launch_stream_merge(const ReduceParams& p, hipStream_t stream) {
   const dim3 grid((pairs + 3) / 4), block(256);
   if (p.head_dim == 64) hipLaunchKernelGGL(stream_merge_kernel<64>, grid, block, 0, stream, p);
   else hipLaunchKernelGGL(stream_merge_kernel<128>, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int KVT, int D, int MODE>
+static hipError_t launch_prefill_t(const DecodeParams& p, hipStream_t stream) {
+  constexpr int kPf = ring_depth<KVT, D>();
+  auto kernel = paged_prefill_persistent<KVT, D, kWaves, MODE, kPf>;
+  const int grid = std::max(kXcds, resident_workgroups(kernel, kWaves * 64) / kXcds * kXcds);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int KVT>
+static hipError_t launch_prefill_d(const DecodeParams& p, int head_dim, int mode, hipStream_t s) {
+  if (head_dim == 64)
+    return mode == MODE_FINAL ? launch_prefill_t<KVT, 64, MODE_FINAL>(p, s) : launch_prefill_t<KVT, 64, MODE_PARTIAL>(p, s);
+  return mode == MODE_FINAL ? launch_prefill_t<KVT, 128, MODE_FINAL>(p, s) : launch_prefill_t<KVT, 128, MODE_PARTIAL>(p, s);
+}
+
+hipError_t launch_prefill(const DecodeParams& p, int kv_dtype, int head_dim, int mode, hipStream_t stream) {
+  switch (kv_dtype) {
+    case KV_F32: return launch_prefill_d<KV_F32>(p, head_dim, mode, stream);
+    case KV_F16: return launch_prefill_d<KV_F16>(p, head_dim, mode, stream);
+    case KV_BF16: return launch_prefill_d<KV_BF16>(p, head_dim, mode, stream);
+    case KV_E4M3: return launch_prefill_d<KV_E4M3>(p, head_dim, mode, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_merge(const ReduceParams& p, hipStream_t stream) {
+  const int64_t pairs = static_cast<int64_t>(p.num_query_tokens) * p.num_q_heads;
+  if (pairs == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((pairs + 3) / 4)), block(256);
+  if (p.head_dim == 64) hipLaunchKernelGGL(prefill_merge_kernel<64>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(prefill_merge_kernel<128>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -31,6 +31,11 @@ struct DecodeParams {
   int32_t num_workers;         // waves of the resident grid
   int32_t num_slots;           // B * Hkv + num_workers
   int32_t window;              // sliding window in tokens (0: whole context)
+  // Multi-token step: q and out are [num_query_tokens][Hq][D], partials
+  // [num_query_tokens][Hq][S][D]; sequence b owns rows query_start[b] ..
+  const int32_t* query_start;  // [B + 1]
+  int32_t num_query_tokens;
+  int32_t tokens_per_pack;     // 16 / G
 };
 
 struct ReduceParams {
@@ -43,6 +48,9 @@ struct ReduceParams {
   const int32_t* seq_tiles;
   int32_t num_kv_heads, num_workers, num_slots;
   int32_t window;              // sliding window in tokens (0: whole context)
+  // Multi-token step only.
+  const int32_t* query_start;
+  int32_t num_query_tokens;
 };
 
 struct WriteParams {
@@ -97,6 +105,9 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
 int stream_max_workers(int kv_dtype, int head_dim);
 hipError_t launch_stream(const DecodeParams& p, int kv_dtype, int head_dim, hipStream_t stream);
 hipError_t launch_stream_merge(const ReduceParams& p, hipStream_t stream);
+// Multi-token step: mode 0 one pass to out, 1 partials; then the merge.
+hipError_t launch_prefill(const DecodeParams& p, int kv_dtype, int head_dim, int mode, hipStream_t stream);
+hipError_t launch_prefill_merge(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_kv_write(const WriteParams& p, hipStream_t stream);
 hipError_t launch_quantize_e4m3(const QuantParams& p, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);

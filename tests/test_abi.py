@@ -170,3 +170,24 @@ def test_append_e4m3_validates_before_touching_the_device():
     assert lib.kv_cache_append_e4m3(FAKE, FAKE, FAKE, -1, FAKE, FAKE, FAKE, ctypes.byref(d8), None) == INVALID
     assert lib.kv_cache_append_e4m3(FAKE, FAKE, FAKE, 3, FAKE, FAKE, None, ctypes.byref(d8), None) == INVALID
     assert lib.kv_cache_append_e4m3(None, None, None, 0, None, None, None, ctypes.byref(d8), None) == OK
+
+
+def test_prefill_validates_before_touching_the_device():
+    lib = abi.lib()
+
+    def call(d, n=4, P=0, ws=None, ptr=FAKE, nbytes=0):
+        return lib.paged_prefill_attention(ptr, ptr, ptr, ptr, ptr, ptr, n, 0.125, None, P, ws, nbytes, ptr,
+                                           ctypes.byref(d), None)
+    assert call(desc(num_seqs=2049)) == UNSUPPORTED
+    assert call(desc(sliding_window=8)) == UNSUPPORTED
+    assert call(desc(), P=24) == INVALID
+    assert call(desc(), n=-1) == INVALID
+    assert call(desc(), ptr=None) == INVALID
+    assert call(desc(), P=64) == INVALID                           # partitioned without a workspace
+    assert call(desc(), P=64, ws=ctypes.c_void_p(0x1010), nbytes=1 << 30) == INVALID   # misaligned
+    assert call(desc(), n=0, ptr=None) == OK
+    d = desc(num_seqs=3, num_q_heads=28, num_kv_heads=4, head_dim=128, max_blocks_per_seq=100)
+    S = math.ceil(100 * 16 / 512)
+    rows = 50 * 28 * S
+    assert lib.paged_prefill_workspace_bytes(ctypes.byref(d), 50, 512) == (rows * 4 + 255) // 256 * 256 + rows * 128 * 4
+    assert lib.paged_prefill_workspace_bytes(ctypes.byref(d), 50, 0) == 0

@@ -549,3 +549,92 @@ def test_append_e4m3_fills_a_block_token_by_token():
         torch.cuda.synchronize()
         assert np.array_equal(k_g.cpu().numpy(), k_o) and np.array_equal(v_g.cpu().numpy(), v_o), t
         assert np.array_equal(s_g.cpu().numpy().view(np.uint32), s_o.view(np.uint32)), t
+
+
+# ------------------------------------------------- multi-token (causal) step ---
+
+def _prefill_oracle(w, pool=None):
+    k, v, sc = pool if pool is not None else oracle_pool(w)
+    return ref.prefill_attention(w.q, w.spec.q_dtype, k, v, w.spec.kv_dtype, w.block_tables, w.context_lens,
+                                 w.query_start, w.scale, sc)
+
+
+def _prefill_gpu(w, pool, P, out_dtype=torch.float32):
+    from paged_kv_gqa_cache_amd import abi
+    k, v, sc = pool
+    q = to_dev(w.q, w.spec.q_dtype)
+    return abi.paged_prefill_attention(q, k, v, torch.from_numpy(w.block_tables).cuda(),
+                                       torch.from_numpy(w.context_lens).cuda(),
+                                       torch.from_numpy(w.query_start).cuda(), w.scale, sc, partition_size=P,
+                                       out_dtype=out_dtype)
+
+
+PREFILL_SHAPES = [
+    dict(),                                                                  # G = 7: 2 tokens per pack
+    dict(num_q_heads=16, num_kv_heads=4, head_dim=64),                      # G = 4: 4 tokens
+    dict(num_q_heads=4, num_kv_heads=4),                                    # G = 1: 16 tokens
+    dict(num_q_heads=32, num_kv_heads=2),                                   # G = 16: 1 token
+    dict(num_q_heads=8, num_kv_heads=4, q_dtype="f16", kv_dtype="f16"),     # G = 2
+    dict(q_dtype="f32", kv_dtype="f32", head_dim=64, num_q_heads=12, num_kv_heads=4),
+    dict(q_dtype="f16", kv_dtype="e4m3"),
+]
+
+
+@pytest.mark.parametrize("P", [0, 64, 512])
+@pytest.mark.parametrize("kw", PREFILL_SHAPES)
+def test_prefill_matches_oracle(kw, P):
+    _announce("prefill", kw, P)
+    w = workloads.generate("qwen25_7b_chunk", num_seqs=5, lengths=("uniform", 1, 700),
+                           query_tokens=("uniform", 1, 40), **kw)
+    assert max_err(_prefill_gpu(w, gpu_pool(w), P), _prefill_oracle(w)) <= TOL
+
+
+def test_prefill_with_one_new_token_is_decode_bitwise():
+    _announce("prefill n=1")
+    from paged_kv_gqa_cache_amd import abi
+    w = workloads.generate("qwen25_7b_chunk", num_seqs=6, lengths=("uniform", 1, 900), query_tokens=("uniform", 1, 1))
+    pool = gpu_pool(w)
+    got = _prefill_gpu(w, pool, 0)
+    q, tables, lens = inputs(w)
+    dec = abi.paged_decode_attention(q, pool[0], pool[1], tables, lens, w.scale, None)
+    assert torch.equal(got, dec)
+    assert max_err(got, _prefill_oracle(w)) <= TOL
+
+
+def test_prefill_whole_context_new_and_16bit_output():
+    """Every position new (pure prefill of short prompts), bf16 output equal to
+    the fp32 output rounded, within one ulp."""
+    _announce("prefill full")
+    w = workloads.generate("qwen25_7b_chunk", num_seqs=4, lengths=("uniform", 1, 200),
+                           query_tokens=("uniform", 200, 200))
+    assert np.array_equal(np.diff(w.query_start), w.context_lens)
+    pool = gpu_pool(w)
+    o32 = _prefill_gpu(w, pool, 64)
+    assert max_err(o32, _prefill_oracle(w)) <= TOL
+    o16 = _prefill_gpu(w, pool, 64, torch.bfloat16)
+    r = o32.to(torch.bfloat16)
+    ulp = (r.float().abs() * 2.0 ** -7).clamp_min(1e-30)
+    assert torch.all((o16.float() - r.float()).abs() <= ulp)
+
+
+def test_prefill_full_size_sampled():
+    """The 16-sequence chunked-prefill workload at full size (in the
+    partitioned configuration), checked on three sequences' rows."""
+    _announce("prefill full size")
+    w = workloads.generate("qwen25_7b_chunk")
+    pool = gpu_pool(w)
+    got = _prefill_gpu(w, pool, 512).cpu().numpy()
+    assert np.all(np.isfinite(got))
+    pick = [int(np.argmax(np.diff(w.query_start))), int(np.argmin(w.context_lens)), 5]
+    for b in pick:
+        q0, q1 = int(w.query_start[b]), int(w.query_start[b + 1])
+        sub = workloads.Workload(**{**w.__dict__})
+        sub.q = w.q[q0:q1]
+        sub.block_tables = w.block_tables[b:b + 1]
+        sub.context_lens = w.context_lens[b:b + 1]
+        sub.query_start = np.array([0, q1 - q0], np.int32)
+        used = np.unique(sub.block_tables[sub.block_tables >= 0])
+        keep = np.isin(w.fill_blocks, used)
+        sub.fill_blocks, sub.fill_valid = w.fill_blocks[keep], w.fill_valid[keep]
+        sub.fill_k, sub.fill_v = w.fill_k[keep], w.fill_v[keep]
+        assert float(np.max(np.abs(got[q0:q1] - _prefill_oracle(sub)))) <= TOL, b
