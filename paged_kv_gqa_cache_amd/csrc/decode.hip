@@ -644,11 +644,17 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(const DecodeParam
 
 // Persistent form: as many workgroups as fit on the GPU at once.  Each one
 // first counts the non-empty work items of every sequence (an exclusive
-// prefix sum in LDS), then walks item n = blockIdx.x, + gridDim.x, ... in
-// sequence-major order, mapping n back to (sequence, kv head, partition) by
-// binary search.  No workgroup is launched for an empty partition.
+// prefix sum in LDS), then walks its share of the items, mapping each back
+// to (sequence, kv head, partition).  No workgroup is launched for an empty
+// partition.
 constexpr int kMaxSeqsPersistent = 2048;
-constexpr int kXcds = 8;   // accelerator complex dies of an MI355X
+constexpr int kXcds = 8;       // accelerator complex dies of an MI355X
+// Neighbouring sequences whose first partitions run together.  The split
+// mode keeps one: there the last partition of a (sequence, kv head) merges
+// them all, so a sequence's partitions are best finished close together
+// (measured ~4% faster on a 32-sequence layer without shared prefixes).
+template <int MODE>
+constexpr int seq_block() { return MODE == MODE_SPLIT ? 1 : 8; }
 
 template <int KVT, int D, int NW, int MODE, int PF>
 __global__ __launch_bounds__(NW * 64) void paged_decode_persistent(const DecodeParams p) {
@@ -703,18 +709,51 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_persistent(const DecodeP
   const int per_xcd = gridDim.x / kXcds;
   const int lo = static_cast<int>(static_cast<int64_t>(N) * xcd / kXcds);
   const int hi = static_cast<int>(static_cast<int64_t>(N) * (xcd + 1) / kXcds);
-  // Item n -> (sequence, kv head, partition): last b with s_cum[b] <= n.
+  // Item n -> (sequence, kv head, partition).  Sequences go in blocks of
+  // kSeqBlock neighbours; inside a block the first partitions of all its
+  // sequences (every kv head) come first, then each sequence's remaining
+  // partitions.  Neighbouring sequences that share a prompt (parallel
+  // samples, beams) then read their shared leading blocks at the same time,
+  // through one XCD's L2, instead of one sequence at a time after the L2 has
+  // moved on.
+  constexpr int kSeqBlock = seq_block<MODE>();
   auto locate = [&](int n, int& b, int& h, int& part) {
-    int lo_b = 0, hi_b = B;
-    while (hi_b - lo_b > 1) {
-      const int mid = (lo_b + hi_b) >> 1;
-      if (s_cum[mid] <= n) lo_b = mid;
-      else hi_b = mid;
+    int lo_m = 0, hi_m = (B + kSeqBlock - 1) / kSeqBlock;
+    while (hi_m - lo_m > 1) {
+      const int mid = (lo_m + hi_m) >> 1;
+      if (s_cum[mid * kSeqBlock] <= n) lo_m = mid;
+      else hi_m = mid;
     }
-    b = lo_b;
-    const int local = n - s_cum[b];
-    h = local / s_np[b];
-    part = local % s_np[b];
+    const int b0 = lo_m * kSeqBlock;
+    const int b1 = min(B, b0 + kSeqBlock);
+    int local = n - s_cum[b0];
+    int firsts = 0;   // items of the block's first partitions
+    for (int bb = b0; bb < b1; ++bb) firsts += (s_np[bb] > 0) ? Hkv : 0;
+    b = b1 - 1;
+    h = 0;
+    part = 0;
+    if (local < firsts) {
+      int k = local / Hkv;
+      for (int bb = b0; bb < b1; ++bb) {
+        if (s_np[bb] > 0 && k-- == 0) {
+          b = bb;
+          break;
+        }
+      }
+      h = local % Hkv;
+      return;
+    }
+    local -= firsts;
+    for (int bb = b0; bb < b1; ++bb) {
+      const int rest = (s_np[bb] > 0) ? (s_np[bb] - 1) * Hkv : 0;
+      if (local < rest) {
+        b = bb;
+        h = local / (s_np[bb] - 1);
+        part = 1 + local % (s_np[bb] - 1);
+        return;
+      }
+      local -= rest;
+    }
   };
   ItemPrefetch<KVT, D> cur, nxt;
   int b, h, part, b2, h2, part2;
