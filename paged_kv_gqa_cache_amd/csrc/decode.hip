@@ -7,7 +7,16 @@
 // row "PagedAttention V2"; "LLM Serving Kernels", section "Projects", row 04:
 // page tables, GQA/MQA, online softmax).  In split mode each partition of
 // the context yields a normalised partial output and its log-sum-exp; the
-// reduce kernel merges them (flash-decoding).
+// reduce kernel merges them (flash-decoding).  Also here: the same with a
+// sliding window (only the last W positions), a balanced schedule (equal
+// 16-token tile shares per wave, split at any point, merged by log-sum-exp),
+// and the multi-token step (several new tokens per sequence, causal).
+//
+// Kernels: paged_decode_kernel / paged_decode_persistent (one pass, split
+// partials, or split with an in-kernel merge), paged_decode_stream +
+// stream_merge_kernel (balanced schedule), paged_prefill_persistent +
+// prefill_merge_kernel (multi-token step), lse_merge_kernel (partition
+// merge of the split pair).
 //
 // How, on CDNA4:
 //  * One workgroup = NW wave64s = one (partition, kv head, sequence).  The
