@@ -18,7 +18,11 @@ stream the kernel runs on (events created with hipEventDisableSystemFence,
 which costs about 1 us per step instead of about 5).  ``cpu_baseline`` is the
 float64 oracle on the host, one thread, on the same batch.  A second workload
 (the B=32 Qwen2.5-1.5B-shaped layer with its new-token write) is timed in the
-same run and reported as ``b32``.
+same run and reported as ``b32``.  The other rows of the path (FP8 E4M3
+decode, the sliding window, the multi-token step, the E4M3 quantiser and
+append, the block copy and the slot write) are measured on their own
+workloads in the same run and reported under ``rows``, each against the
+roofline that bounds it.
 """
 from __future__ import annotations
 
@@ -218,6 +222,158 @@ def cpu_baseline(name: str):
                       f"times (~{sum(times):.0f} s); median {t * 1e3:.0f} ms per step"}
 
 
+def time_calls(fn, n: int, warmup: int = 3) -> float:
+    """Average milliseconds per call of ``fn`` (which launches on the current
+    stream), from HIP events on that stream around n back-to-back calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    ev = HipEvents(2)
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    ev.record(0, stream)
+    for _ in range(n):
+        fn()
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(0, 1) / n
+    ev.close()
+    return ms
+
+
+def hbm_row(bytes_per_call: int, ms: float, what: str) -> dict:
+    gbps = bytes_per_call / (ms * 1e-3) / 1e9
+    return {"us": round(ms * 1e3, 2), "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes": bytes_per_call, "bytes_are": what}
+
+
+def measure_rows(args) -> dict:
+    """The other rows of the path, each on its own workload, through the C ABI.
+    Attention rows rotate layer pools like the headline (cold K/V); the cache
+    maintenance rows are timed back to back (warm), as labelled."""
+    import numpy as np
+    import torch
+    from paged_kv_gqa_cache_amd import abi, workloads
+    from paged_kv_gqa_cache_amd.pool import gpu_pool, to_dev
+
+    rows = {}
+    steps, warm = max(10, args.steps // 2), max(3, args.warmup // 2)
+
+    # FP8 E4M3 decode (per-(block, kv head) scales) and the sliding window:
+    # balanced schedule, kernel time = stream kernel + merge (both in the events).
+    for key, name, P in (("fp8_e4m3_decode", "qwen25_7b_fp8", 512), ("sliding_window", "gemma_sliding", 512)):
+        r = Runner(name, args.layers, P, "balanced")
+        t, part = r.run(steps, warm)
+        ms = sum(part) / len(part)
+        row = hbm_row(r.unique_bytes, ms, "unique K/V (+ E4M3 scales) bytes read per step")
+        row.update({"workload": f"{name}: {DESCRIPTIONS[name]}", "path": "balanced",
+                    "us_per_step": round(t * 1e6, 2), "step_GBps": round(r.unique_bytes / t / 1e9, 1)})
+        rows[key] = row
+        if name == "qwen25_7b_fp8":
+            # Bulk quantiser on the same layer: fp32 blocks in, codes + scales out.
+            w, sp = r.w, r.spec
+            ksrc = torch.from_numpy(w.fill_k.view(np.float32)).cuda()
+            vsrc = torch.from_numpy(w.fill_v.view(np.float32)).cuda()
+            ids = torch.from_numpy(w.fill_blocks.astype(np.int32)).cuda()
+            valid = torch.from_numpy(w.fill_valid.astype(np.int32)).cuda()
+            k, v, sc = r.pools[0]
+            ms = time_calls(lambda: abi.kv_cache_quantize_e4m3(ksrc, vsrc, ids, valid, k, v, sc), 10)
+            nblk = int(ids.numel())
+            moved = 2 * (ksrc.numel() * 4 + nblk * 16 * sp.num_kv_heads * sp.head_dim) + 2 * nblk * sp.num_kv_heads * 4
+            rows["e4m3_bulk_quantise"] = hbm_row(moved, ms, "fp32 K/V read + E4M3 codes and scales written")
+            rows["e4m3_bulk_quantise"]["workload"] = f"{nblk} blocks x {sp.num_kv_heads} kv heads x 16 tokens x {sp.head_dim}, K and V"
+            # Append of one token per sequence into its last block (scale growth + re-encode).
+            T = sp.num_seqs
+            rng = np.random.default_rng(7)
+            blocks = rng.permutation(w.num_blocks)[:T]
+            slots = torch.tensor(blocks * 16 + 9, dtype=torch.int64, device="cuda")
+            kn = torch.from_numpy(rng.standard_normal((T, sp.num_kv_heads, sp.head_dim), dtype=np.float32) * 4).cuda()
+            vn = torch.from_numpy(rng.standard_normal((T, sp.num_kv_heads, sp.head_dim), dtype=np.float32) * 4).cuda()
+            ms = time_calls(lambda: abi.kv_cache_append_e4m3(kn, vn, slots, k, v, sc), 50)
+            rows["e4m3_append"] = {"us": round(ms * 1e3, 2), "bound": "latency",
+                                   "workload": f"{T} tokens (one per sequence) into distinct blocks at offset 9, "
+                                               f"{sp.num_kv_heads} kv heads x {sp.head_dim}; every block re-read "
+                                               "and re-encoded when its scale grows"}
+        del r
+        torch.cuda.empty_cache()
+
+    # Multi-token step: chunked prefill (1-256 new tokens per sequence) and
+    # speculative verification (4 tokens per sequence).
+    for key, kw, P in (("chunked_prefill", {}, 1024),
+                       ("spec_verify_4", dict(num_seqs=64, query_tokens=("uniform", 4, 4)), 512)):
+        w = workloads.generate("qwen25_7b_chunk", **kw)
+        sp = w.spec
+        base = gpu_pool(w)
+        pools = [base] + [tuple(None if x is None else x.clone() for x in base) for _ in range(args.layers - 1)]
+        q = to_dev(w.q, sp.q_dtype)
+        tables = torch.from_numpy(w.block_tables).cuda()
+        lens = torch.from_numpy(w.context_lens).cuda()
+        qs = torch.from_numpy(w.query_start).cuda()
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+        ws = abi.prefill_workspace(q, base[0], tables, P)
+        it = [0]
+
+        def call():
+            k, v, sc = pools[it[0] % len(pools)]
+            it[0] += 1
+            abi.paged_prefill_attention(q, k, v, tables, lens, qs, w.scale, sc, P, ws, out=out)
+
+        ms = time_calls(call, steps)
+        n = np.diff(w.query_start).astype(np.int64)
+        L = w.context_lens.astype(np.int64)
+        attended = int(sum(((L[b] - n[b]) + np.arange(n[b]) + 1).sum() for b in range(len(L))))
+        flops = attended * sp.num_q_heads * 4 * sp.head_dim
+        kvb = workloads.kv_bytes(w, unique=True)
+        tf = flops / (ms * 1e-3) / 1e12
+        desc = (f"qwen25_7b_chunk: {len(L)} seqs, 28 Q / 4 KV heads, head_dim 128, bf16, context uniform "
+                f"[512, 4096], {int(n.sum())} new query rows ({int(n.min())}-{int(n.max())} per sequence), "
+                f"causal within the new tokens, P = {P}")
+        if key == "chunked_prefill":
+            rows[key] = {"us": round(ms * 1e3, 2), "bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0,
+                         "unit": "TFLOP/s", "frac": round(tf / 2500.0, 4),
+                         "flops": flops, "flops_are": "4 * head_dim per (query row, query head, attended position)",
+                         "kv_GBps": round(kvb / (ms * 1e-3) / 1e9, 1), "workload": desc}
+        else:
+            row = hbm_row(kvb, ms, "unique K/V bytes read per step")
+            row.update({"TFLOPs": round(tf, 1), "workload": desc})
+            rows[key] = row
+        del pools, base
+        torch.cuda.empty_cache()
+
+    # Block copy (copy-on-write / beam fork): 4096 (source, destination)
+    # pairs of bf16 blocks, 4 kv heads x head_dim 128, four disjoint pair
+    # sets in turn.
+    NB, Hkv, D, npairs = 40960, 4, 128, 4096
+    kc = torch.zeros((NB, Hkv, 16 * D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    rng = np.random.default_rng(11)
+    perm = rng.permutation(NB)
+    maps = [torch.tensor(np.stack([perm[i * 2 * npairs:i * 2 * npairs + npairs],
+                                   perm[i * 2 * npairs + npairs:(i + 1) * 2 * npairs]], 1).astype(np.int32),
+                         device="cuda") for i in range(4)]
+    it = [0]
+
+    def copy_call():
+        abi.kv_cache_copy_blocks(maps[it[0] % 4], kc, vc)
+        it[0] += 1
+
+    ms = time_calls(copy_call, 20)
+    moved = 2 * 2 * npairs * Hkv * 16 * D * 2
+    rows["copy_blocks"] = hbm_row(moved, ms, "K and V blocks read + written")
+    rows["copy_blocks"]["workload"] = f"{npairs} block pairs of {Hkv} kv heads x 16 tokens x {D} bf16, K and V"
+    del kc, vc, maps
+
+    # New-token slot write of the B=32 layer (32 tokens, 2 kv heads, f16).
+    w = workloads.generate(SECONDARY)
+    k, v, _ = gpu_pool(w, with_new_tokens=False)
+    nk, nv = to_dev(w.new_k, w.spec.kv_dtype), to_dev(w.new_v, w.spec.kv_dtype)
+    slots = torch.from_numpy(w.new_slots).cuda()
+    ms = time_calls(lambda: abi.kv_cache_write(nk, nv, slots, k, v), 50)
+    rows["kv_slot_write"] = {"us": round(ms * 1e3, 2), "bound": "latency",
+                             "workload": f"{SECONDARY}: 32 new tokens x 2 kv heads x 128, f16"}
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +384,8 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="layer pools rotated through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the other rows of the path (FP8, window, multi-token, quantise, append, copy, write)")
     ap.add_argument("--path", choices=["pair", "fused", "balanced"], default="pair",
                     help="partial + reduce kernels, the one-launch split with in-kernel merge, or "
                          "equal tile shares per wave + merge")
@@ -271,6 +429,10 @@ def main():
                "seqs_layers_per_s": round(r2.spec.num_seqs / t2, 1)}
         del r2
 
+    rows = None
+    if not args.no_rows and args.workload == HEADLINE:
+        rows = measure_rows(args)
+
     line = {
         "metric": "paged GQA decode attn: KV-read HBM GB/s (% of peak) + us/step at B=32/128",
         "value": round(value, 1),
@@ -306,6 +468,7 @@ def main():
                        "balanced": "paged_decode_stream + stream_merge_kernel (both inside the events)"}[args.path],
         },
         "b32": b32,
+        "rows": rows,
         "kernel_source_digest": digest,
         "library": abi.version(),
     }

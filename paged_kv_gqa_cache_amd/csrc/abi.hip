@@ -99,15 +99,14 @@ SplitLayout split_layout(const pkv_desc* d, int64_t s) {
 
 // Balanced workspace: [seq_tiles int32 B+1 | pad to 256][tmp_lse f32 G*slots | pad]
 // [tmp_out f32 G*slots*D], slots = B*Hkv + the resident grid's wave count.
-constexpr int kMaxSeqsBalanced = 2048;
 struct BalancedLayout {
   int64_t slots, lse_off, out_off, total;
   int32_t workers;
 };
 int check_balanced(const pkv_desc* d) {
-  if (d->num_seqs > kMaxSeqsBalanced)
-    return fail(PKV_ERR_UNSUPPORTED, "balanced schedule takes at most %d sequences (got %d)", kMaxSeqsBalanced,
-                d->num_seqs);
+  if (d->num_seqs > pkv::kMaxSeqsPersistent)
+    return fail(PKV_ERR_UNSUPPORTED, "balanced schedule takes at most %d sequences (got %d)",
+                pkv::kMaxSeqsPersistent, d->num_seqs);
   if (static_cast<int64_t>(d->num_seqs) * d->num_kv_heads * d->max_blocks_per_seq > 0x7FFFFFFFLL)
     return fail(PKV_ERR_INVALID_ARG, "num_seqs * num_kv_heads * max_blocks_per_seq exceeds 2^31 - 1");
   return PKV_OK;
@@ -417,8 +416,9 @@ int paged_prefill_attention(const void* q, const void* k_cache, const void* v_ca
                             int64_t workspace_bytes, void* out, const pkv_desc* desc, void* stream) {
   if (int e = check_desc(desc, true)) return e;
   if (int e = check_attn_types(desc, kv_scales)) return e;
-  if (desc->num_seqs > 2048)
-    return fail(PKV_ERR_UNSUPPORTED, "multi-token step takes at most 2048 sequences (got %d)", desc->num_seqs);
+  if (desc->num_seqs > pkv::kMaxSeqsPersistent)
+    return fail(PKV_ERR_UNSUPPORTED, "multi-token step takes at most %d sequences (got %d)",
+                pkv::kMaxSeqsPersistent, desc->num_seqs);
   if (desc->sliding_window != 0) return fail(PKV_ERR_UNSUPPORTED, "multi-token step has no sliding window");
   if (partition_size != 0)
     if (int e = check_partition(partition_size)) return e;

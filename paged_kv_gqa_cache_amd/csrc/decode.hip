@@ -406,6 +406,10 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int 
   // A load past the last block still issues, through a zero-size
   // descriptor (reads 0, no memory traffic), so the loop has no
   // conditional loads and each wait covers exactly the tile it needs.
+  // A decode step reads each K/V tile once, so its loads are non-temporal.
+  // In the multi-token step (CAUSAL) every pack of a sequence's query rows
+  // reads the same tiles again, so they stay ordinary, cacheable loads.
+  constexpr int kTilePolicy = CAUSAL ? 0 : kStreamLoad;
   // E4M3: the block's K and V scales ride in the ring with its tile, loaded
   // just before the tile's codes, so the wait for a tile covers its scales
   // and never the tiles prefetched after it.
@@ -421,9 +425,9 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int 
     const auto kr = make_tile_rsrc(kcache + tile, valid ? TILE : 0);
     const auto vr = make_tile_rsrc(vcache + tile, valid ? TILE : 0);
 #pragma unroll
-    for (int m = 0; m < NL; ++m) kt[m] = buffer_ld16(kr, lane_off[m]);
+    for (int m = 0; m < NL; ++m) kt[m] = buffer_ld16_policy<kTilePolicy>(kr, lane_off[m]);
 #pragma unroll
-    for (int m = 0; m < NL; ++m) vt[m] = buffer_ld16(vr, lane_off[m]);
+    for (int m = 0; m < NL; ++m) vt[m] = buffer_ld16_policy<kTilePolicy>(vr, lane_off[m]);
   };
 
   auto process = [&](const u32x4 (&kt)[NL], u32x4 (&vt)[NL], float ksc, float vsc, int i) {
@@ -656,7 +660,6 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(const DecodeParam
 // prefix sum in LDS), then walks its share of the items, mapping each back
 // to (sequence, kv head, partition).  No workgroup is launched for an empty
 // partition.
-constexpr int kMaxSeqsPersistent = 2048;
 constexpr int kXcds = 8;       // accelerator complex dies of an MI355X
 // Neighbouring sequences whose first partitions run together.  The split
 // mode keeps one: there the last partition of a (sequence, kv head) merges

@@ -67,71 +67,77 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const WriteParams p) {
   for (int i = 0; i < X; ++i) vt[v_tile_elem(off, c * X + i, N)] = vals[i];
 }
 
-// One workgroup (D threads) per (source block, kv head, K-or-V).  Thread i
-// produces the i-th 16-byte chunk of the destination tile:
-//   K: chunk (c, t) = 16 codes of token t, dims [16c, 16c+16);
-//   V: chunk (m, g, r) = codes of dims 64m + 16q + r (q = 0..3) for tokens
-//      4g..4g+3, byte 4q + j for token 4g + j.
+// One wave per (block, kv head, K or V) tile; a workgroup takes four
+// consecutive tiles, ordered (block, K or V, kv head), so the kv heads of a
+// block sit side by side and the workgroup's loads cover whole source rows.
+// Each lane loads 16 bytes (4 consecutive dims of one token) at a time, the
+// wave takes the tile's amax, and the codes go into an LDS image of the tile
+// in its cache layout, which the wave then stores with 16-byte writes.
 // scale = fp32(amax / 448) over the block's valid slots (1 if amax is 0);
 // code = nearest-even E4M3 of clamp(fp32(x / scale), -448, 448); slots at or
 // past valid_tokens get code 0.
-__global__ __launch_bounds__(128) void quantize_e4m3_kernel(const QuantParams p) {
-  const int i = blockIdx.x;
-  const int h = blockIdx.y;
-  const bool is_v = blockIdx.z != 0;
-  const int tid = threadIdx.x;
-  const int D = p.head_dim;
-  const int valid = max(0, min(p.valid_tokens[i], kBlockSize));
-  const float* src = is_v ? p.v_src : p.k_src;
-  auto at = [&](int t, int d) -> float {
-    return src[((static_cast<size_t>(i) * kBlockSize + t) * p.num_kv_heads + h) * D + d];
-  };
-
-  float x[16];
-  bool ok[16];
+template <int D>
+__global__ __launch_bounds__(256) void quantize_e4m3_kernel(const QuantParams p) {
+  constexpr int TB = kBlockSize * D;         // bytes of codes in one tile
+  constexpr int NJ = kBlockSize * D / 256;   // 16-byte loads per lane
+  constexpr int C4 = D / 4;                  // 16-byte pieces per source row
+  __shared__ __align__(16) unsigned char img[4][TB];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int Hkv = p.num_kv_heads;
+  const int64_t ntiles = static_cast<int64_t>(p.num_src_blocks) * Hkv * 2;
+  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + wid;
+  const bool live = tile < ntiles;   // wave-uniform
+  const int h = live ? static_cast<int>(tile % Hkv) : 0;
+  const bool is_v = live && ((tile / Hkv) % 2) != 0;
+  const int i = live ? static_cast<int>(tile / (2 * Hkv)) : 0;
+  float scale = 1.0f;
+  if (live) {
+    const int valid = max(0, min(p.valid_tokens[i], kBlockSize));
+    const float* src = (is_v ? p.v_src : p.k_src) + (static_cast<size_t>(i) * kBlockSize * Hkv + h) * D;
+    u32x4 x[NJ];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    int t, d;
-    if (!is_v) {
-      t = tid % 16;
-      d = 16 * (tid / 16) + k;
-    } else {
-      const int m = tid / 64, g = (tid / 16) % 4, r = tid % 16;
-      t = 4 * g + (k % 4);
-      d = 64 * m + 16 * (k / 4) + r;
+    for (int j = 0; j < NJ; ++j) {
+      const int e = j * 64 + lane;
+      const int t = e / C4;
+      x[j] = t < valid ? ld16(src + static_cast<size_t>(t) * Hkv * D + 4 * (e % C4)) : u32x4{0u, 0u, 0u, 0u};
     }
-    ok[k] = t < valid;
-    x[k] = ok[k] ? at(t, d) : 0.f;
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fabsf(__uint_as_float(x[j][k])));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    scale = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = j * 64 + lane;
+      const int t = e / C4;
+      const int d = 4 * (e % C4);
+      uint32_t code[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float y = fminf(fmaxf(__uint_as_float(x[j][k]) / scale, -448.0f), 448.0f);
+        code[k] = t < valid ? f32_to_e4m3(y) : 0u;
+      }
+      if (!is_v) {   // K: dims d..d+3 of token t are 4 consecutive bytes of one 16-byte chunk
+        *reinterpret_cast<uint32_t*>(&img[wid][((d / 16) * kBlockSize + t) * 16 + d % 16]) =
+            code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+      } else {       // V: each dim lands in its own chunk (tokens are the fast index there)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) img[wid][v_tile_elem(t, d + k, 4)] = static_cast<unsigned char>(code[k]);
+      }
+    }
   }
-
-  float amax = 0.f;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(x[k]));
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  __shared__ float sm[2];
-  if ((tid & 63) == 0) sm[tid >> 6] = amax;
   __syncthreads();
-  amax = sm[0];
-  if (blockDim.x > 64) amax = fmaxf(amax, sm[1]);
-  const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
-
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (live) {
+    const int blk = p.block_ids[i];
+    char* dst = static_cast<char*>(is_v ? p.v_cache : p.k_cache) + (static_cast<size_t>(blk) * Hkv + h) * TB;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const float y = fminf(fmaxf(x[k] / scale, -448.0f), 448.0f);
-    const uint32_t code = ok[k] ? f32_to_e4m3(y) : 0u;
-    w[k / 4] |= code << (8 * (k % 4));
+    for (int off = lane * 16; off < TB; off += 1024) st16(dst + off, *reinterpret_cast<const u32x4*>(&img[wid][off]));
+    if (lane == 0) p.kv_scales[((is_v ? static_cast<size_t>(p.num_blocks) : 0) + blk) * Hkv + h] = scale;
   }
-  const int blk = p.block_ids[i];
-  char* cache = static_cast<char*>(is_v ? p.v_cache : p.k_cache);
-  const size_t tile = (static_cast<size_t>(blk) * p.num_kv_heads + h) * kBlockSize * D;
-  size_t byte;
-  if (!is_v) byte = (static_cast<size_t>(tid / 16) * kBlockSize + tid % 16) * 16;
-  else byte = static_cast<size_t>(tid) * 16;
-  st16(cache + tile + byte, u32x4{w[0], w[1], w[2], w[3]});
-  if (tid == 0)
-    p.kv_scales[((is_v ? static_cast<size_t>(p.num_blocks) : 0) + blk) * p.num_kv_heads + h] = scale;
 }
 
 // One workgroup (D threads) per (token, kv head, K-or-V); thread d owns dim
@@ -196,8 +202,8 @@ hipError_t launch_append_e4m3(const AppendParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// One thread per 16-byte chunk of a block (a block's Hkv tiles are one
-// contiguous run), grid (chunks / 256, pairs, K-or-V).  Pairs naming a block
+// A block's Hkv tiles are one contiguous run of 16-byte chunks; grid
+// (chunks / 1024, pairs, K-or-V), four chunks per thread.  Pairs naming a block
 // outside the pool are skipped.  The first threads of each (pair, K-or-V)
 // (blockIdx.x = 0) also copy that block's Hkv scales of an E4M3 pool.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(const CopyParams p) {
@@ -207,11 +213,20 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const CopyParams p) {
   const int dst = p.block_mapping[2 * pair + 1];
   if (src < 0 || src >= p.num_blocks || dst < 0 || dst >= p.num_blocks) return;
   char* cache = static_cast<char*>(is_v ? p.v_cache : p.k_cache);
-  const int64_t chunk = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (chunk < p.block_bytes / 16) {
-    const u32x4 x = ld16(cache + static_cast<size_t>(src) * p.block_bytes + chunk * 16);
-    st16(cache + static_cast<size_t>(dst) * p.block_bytes + chunk * 16, x);
-  }
+  const u32x4* from = reinterpret_cast<const u32x4*>(cache + static_cast<size_t>(src) * p.block_bytes);
+  u32x4* to = reinterpret_cast<u32x4*>(cache + static_cast<size_t>(dst) * p.block_bytes);
+  // Each thread moves chunks c0, c0 + 256, c0 + 512, c0 + 768 of this
+  // workgroup's 1024-chunk span: all four loads issue before the stores.
+  // Both sides stream (non-temporal): the copy touches each byte once.
+  const int64_t nchunks = p.block_bytes / 16;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 1024 + threadIdx.x;
+  u32x4 x[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (c0 + 256 * u < nchunks) x[u] = __builtin_nontemporal_load(from + c0 + 256 * u);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (c0 + 256 * u < nchunks) __builtin_nontemporal_store(x[u], to + c0 + 256 * u);
   if (p.kv_scales != nullptr && blockIdx.x == 0) {
     float* sc = p.kv_scales + (is_v ? static_cast<size_t>(p.num_blocks) * p.num_kv_heads : 0);
     for (int h = threadIdx.x; h < p.num_kv_heads; h += 256)
@@ -222,7 +237,7 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const CopyParams p) {
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream) {
   if (p.num_pairs == 0) return hipSuccess;
   const int64_t chunks = p.block_bytes / 16;
-  const dim3 grid(static_cast<unsigned>((chunks + 255) / 256), static_cast<unsigned>(p.num_pairs), 2), block(256);
+  const dim3 grid(static_cast<unsigned>((chunks + 1023) / 1024), static_cast<unsigned>(p.num_pairs), 2), block(256);
   hipLaunchKernelGGL(copy_blocks_kernel, grid, block, 0, stream, p);
   return hipGetLastError();
 }
@@ -239,8 +254,11 @@ hipError_t launch_kv_write(const WriteParams& p, hipStream_t stream) {
 
 hipError_t launch_quantize_e4m3(const QuantParams& p, hipStream_t stream) {
   if (p.num_src_blocks == 0) return hipSuccess;
-  const dim3 grid(p.num_src_blocks, p.num_kv_heads, 2), block(p.head_dim);
-  hipLaunchKernelGGL(quantize_e4m3_kernel, grid, block, 0, stream, p);
+  const int64_t tiles = static_cast<int64_t>(p.num_src_blocks) * p.num_kv_heads * 2;
+  const dim3 grid(static_cast<unsigned>((tiles + 3) / 4)), block(256);
+  if (p.head_dim == 128) hipLaunchKernelGGL(quantize_e4m3_kernel<128>, grid, block, 0, stream, p);
+  else if (p.head_dim == 64) hipLaunchKernelGGL(quantize_e4m3_kernel<64>, grid, block, 0, stream, p);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

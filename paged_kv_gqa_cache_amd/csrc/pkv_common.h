@@ -50,6 +50,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_tile_rsrc(const void* bas
 __device__ __forceinline__ u32x4 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// Cache-policy operand marking a load non-temporal (the `nt` bit): the lines
+// are streamed through L2 and the memory-side cache with early eviction.  On
+// gfx950 a plain read stream reaches ~6.3 TB/s and an `nt` one ~7.1 TB/s.
+constexpr int kStreamLoad = 2;
+template <int POLICY>
+__device__ __forceinline__ u32x4 buffer_ld16_policy(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
+}
 
 // Cache-policy operand of buffer loads/stores selecting device (agent)
 // scope on gfx950: the access is coherent across the XCDs' L2 caches.

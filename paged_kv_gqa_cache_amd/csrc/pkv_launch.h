@@ -10,6 +10,11 @@
 
 namespace pkv {
 
+// Sequences whose per-sequence tables fit in a persistent workgroup's LDS.
+// The decode kernels fall back to one workgroup per item above it; the
+// balanced schedule and the multi-token step reject larger batches.
+constexpr int kMaxSeqsPersistent = 2048;
+
 struct DecodeParams {
   const void* q;               // [B][Hq][D]
   const void* k_cache;         // [NB][Hkv][tile]

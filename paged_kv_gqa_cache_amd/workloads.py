@@ -94,7 +94,7 @@ SPECS = {
                                 ("uniform", 512, 4096), new_token_write=True, partition_size=512),
     "qwen25_7b_prefix": WorkloadSpec("qwen25_7b_prefix", 1004, 128, 28, 4, 128, "bf16", "bf16",
                                      ("lognormal", 1024, 1.0, 16, 32768), prefix_group=8,
-                                     prefix_blocks=32, partition_size=512),
+                                     prefix_blocks=32, partition_size=768),
     "qwen25_7b_fp8": WorkloadSpec("qwen25_7b_fp8", 1005, 64, 28, 4, 128, "f16", "e4m3",
                                   ("fixed", 8192), partition_size=1024),
     "gemma_sliding": WorkloadSpec("gemma_sliding", 1006, 64, 32, 16, 128, "bf16", "bf16",

@@ -95,7 +95,9 @@ def test_kv_cache_write_is_bit_exact(name):
 
 
 @pytest.mark.parametrize("kw", [dict(num_seqs=3, lengths=("uniform", 1, 700)),
-                                dict(num_seqs=2, lengths=("uniform", 1, 300), head_dim=64)])
+                                dict(num_seqs=2, lengths=("uniform", 1, 300), head_dim=64),
+                                # 3 kv heads, 137 blocks: 822 tiles leave two idle waves in the last workgroup
+                                dict(num_seqs=4, lengths=("uniform", 1, 900), num_q_heads=6, num_kv_heads=3)])
 def test_quantize_e4m3_is_bit_exact(kw):
     _announce("quantize", kw)
     w = workloads.generate("qwen25_7b_fp8", **kw)
