@@ -247,10 +247,15 @@ def hbm_row(bytes_per_call: int, ms: float, what: str) -> dict:
             "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes": bytes_per_call, "bytes_are": what}
 
 
-def measure_rows(args) -> dict:
+ROW_NAMES = ("fp8_e4m3_decode", "e4m3_bulk_quantise", "e4m3_append", "sliding_window", "chunked_prefill",
+             "spec_verify_4", "copy_blocks", "kv_slot_write")
+
+
+def measure_rows(args, only=None) -> dict:
     """The other rows of the path, each on its own workload, through the C ABI.
     Attention rows rotate layer pools like the headline (cold K/V); the cache
-    maintenance rows are timed back to back (warm), as labelled."""
+    maintenance rows are timed back to back (warm), as labelled.  ``only``
+    limits the run to the named rows."""
     import numpy as np
     import torch
     from paged_kv_gqa_cache_amd import abi, workloads
@@ -258,17 +263,22 @@ def measure_rows(args) -> dict:
 
     rows = {}
     steps, warm = max(10, args.steps // 2), max(3, args.warmup // 2)
+    want = (lambda k: True) if not only else (lambda k: k in only)
 
     # FP8 E4M3 decode (per-(block, kv head) scales) and the sliding window:
     # balanced schedule, kernel time = stream kernel + merge (both in the events).
     for key, name, P in (("fp8_e4m3_decode", "qwen25_7b_fp8", 512), ("sliding_window", "gemma_sliding", 512)):
+        extra = ("e4m3_bulk_quantise", "e4m3_append") if name == "qwen25_7b_fp8" else ()
+        if not any(want(k) for k in (key,) + extra):
+            continue
         r = Runner(name, args.layers, P, "balanced")
-        t, part = r.run(steps, warm)
-        ms = sum(part) / len(part)
-        row = hbm_row(r.unique_bytes, ms, "unique K/V (+ E4M3 scales) bytes read per step")
-        row.update({"workload": f"{name}: {DESCRIPTIONS[name]}", "path": "balanced",
-                    "us_per_step": round(t * 1e6, 2), "step_GBps": round(r.unique_bytes / t / 1e9, 1)})
-        rows[key] = row
+        if want(key):
+            t, part = r.run(steps, warm)
+            ms = sum(part) / len(part)
+            row = hbm_row(r.unique_bytes, ms, "unique K/V (+ E4M3 scales) bytes read per step")
+            row.update({"workload": f"{name}: {DESCRIPTIONS[name]}", "path": "balanced",
+                        "us_per_step": round(t * 1e6, 2), "step_GBps": round(r.unique_bytes / t / 1e9, 1)})
+            rows[key] = row
         if name == "qwen25_7b_fp8":
             # Bulk quantiser on the same layer: fp32 blocks in, codes + scales out.
             w, sp = r.w, r.spec
@@ -277,11 +287,14 @@ def measure_rows(args) -> dict:
             ids = torch.from_numpy(w.fill_blocks.astype(np.int32)).cuda()
             valid = torch.from_numpy(w.fill_valid.astype(np.int32)).cuda()
             k, v, sc = r.pools[0]
-            ms = time_calls(lambda: abi.kv_cache_quantize_e4m3(ksrc, vsrc, ids, valid, k, v, sc), 10)
             nblk = int(ids.numel())
-            moved = 2 * (ksrc.numel() * 4 + nblk * 16 * sp.num_kv_heads * sp.head_dim) + 2 * nblk * sp.num_kv_heads * 4
-            rows["e4m3_bulk_quantise"] = hbm_row(moved, ms, "fp32 K/V read + E4M3 codes and scales written")
-            rows["e4m3_bulk_quantise"]["workload"] = f"{nblk} blocks x {sp.num_kv_heads} kv heads x 16 tokens x {sp.head_dim}, K and V"
+            if want("e4m3_bulk_quantise"):
+                ms = time_calls(lambda: abi.kv_cache_quantize_e4m3(ksrc, vsrc, ids, valid, k, v, sc), 10)
+                moved = (2 * (ksrc.numel() * 4 + nblk * 16 * sp.num_kv_heads * sp.head_dim)
+                         + 2 * nblk * sp.num_kv_heads * 4)
+                rows["e4m3_bulk_quantise"] = hbm_row(moved, ms, "fp32 K/V read + E4M3 codes and scales written")
+                rows["e4m3_bulk_quantise"]["workload"] = (f"{nblk} blocks x {sp.num_kv_heads} kv heads x 16 tokens "
+                                                          f"x {sp.head_dim}, K and V")
             # Append of one token per sequence into its last block (scale growth + re-encode).
             T = sp.num_seqs
             rng = np.random.default_rng(7)
@@ -289,11 +302,12 @@ def measure_rows(args) -> dict:
             slots = torch.tensor(blocks * 16 + 9, dtype=torch.int64, device="cuda")
             kn = torch.from_numpy(rng.standard_normal((T, sp.num_kv_heads, sp.head_dim), dtype=np.float32) * 4).cuda()
             vn = torch.from_numpy(rng.standard_normal((T, sp.num_kv_heads, sp.head_dim), dtype=np.float32) * 4).cuda()
-            ms = time_calls(lambda: abi.kv_cache_append_e4m3(kn, vn, slots, k, v, sc), 50)
-            rows["e4m3_append"] = {"us": round(ms * 1e3, 2), "bound": "latency",
-                                   "workload": f"{T} tokens (one per sequence) into distinct blocks at offset 9, "
-                                               f"{sp.num_kv_heads} kv heads x {sp.head_dim}; every block re-read "
-                                               "and re-encoded when its scale grows"}
+            if want("e4m3_append"):
+                ms = time_calls(lambda: abi.kv_cache_append_e4m3(kn, vn, slots, k, v, sc), 50)
+                rows["e4m3_append"] = {"us": round(ms * 1e3, 2), "bound": "latency",
+                                       "workload": f"{T} tokens (one per sequence) into distinct blocks at offset "
+                                                   f"9, {sp.num_kv_heads} kv heads x {sp.head_dim}; every block "
+                                                   "re-read and re-encoded when its scale grows"}
         del r
         torch.cuda.empty_cache()
 
@@ -301,6 +315,8 @@ def measure_rows(args) -> dict:
     # speculative verification (4 tokens per sequence).
     for key, kw, P in (("chunked_prefill", {}, 1024),
                        ("spec_verify_4", dict(num_seqs=64, query_tokens=("uniform", 4, 4)), 512)):
+        if not want(key):
+            continue
         w = workloads.generate("qwen25_7b_chunk", **kw)
         sp = w.spec
         base = gpu_pool(w)
@@ -343,34 +359,36 @@ def measure_rows(args) -> dict:
     # Block copy (copy-on-write / beam fork): 4096 (source, destination)
     # pairs of bf16 blocks, 4 kv heads x head_dim 128, four disjoint pair
     # sets in turn.
-    NB, Hkv, D, npairs = 40960, 4, 128, 4096
-    kc = torch.zeros((NB, Hkv, 16 * D), dtype=torch.bfloat16, device="cuda")
-    vc = torch.zeros_like(kc)
-    rng = np.random.default_rng(11)
-    perm = rng.permutation(NB)
-    maps = [torch.tensor(np.stack([perm[i * 2 * npairs:i * 2 * npairs + npairs],
-                                   perm[i * 2 * npairs + npairs:(i + 1) * 2 * npairs]], 1).astype(np.int32),
-                         device="cuda") for i in range(4)]
-    it = [0]
+    if want("copy_blocks"):
+        NB, Hkv, D, npairs = 40960, 4, 128, 4096
+        kc = torch.zeros((NB, Hkv, 16 * D), dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        rng = np.random.default_rng(11)
+        perm = rng.permutation(NB)
+        maps = [torch.tensor(np.stack([perm[i * 2 * npairs:i * 2 * npairs + npairs],
+                                       perm[i * 2 * npairs + npairs:(i + 1) * 2 * npairs]], 1).astype(np.int32),
+                             device="cuda") for i in range(4)]
+        it = [0]
 
-    def copy_call():
-        abi.kv_cache_copy_blocks(maps[it[0] % 4], kc, vc)
-        it[0] += 1
+        def copy_call():
+            abi.kv_cache_copy_blocks(maps[it[0] % 4], kc, vc)
+            it[0] += 1
 
-    ms = time_calls(copy_call, 20)
-    moved = 2 * 2 * npairs * Hkv * 16 * D * 2
-    rows["copy_blocks"] = hbm_row(moved, ms, "K and V blocks read + written")
-    rows["copy_blocks"]["workload"] = f"{npairs} block pairs of {Hkv} kv heads x 16 tokens x {D} bf16, K and V"
-    del kc, vc, maps
+        ms = time_calls(copy_call, 20)
+        moved = 2 * 2 * npairs * Hkv * 16 * D * 2
+        rows["copy_blocks"] = hbm_row(moved, ms, "K and V blocks read + written")
+        rows["copy_blocks"]["workload"] = f"{npairs} block pairs of {Hkv} kv heads x 16 tokens x {D} bf16, K and V"
+        del kc, vc, maps
 
     # New-token slot write of the B=32 layer (32 tokens, 2 kv heads, f16).
-    w = workloads.generate(SECONDARY)
-    k, v, _ = gpu_pool(w, with_new_tokens=False)
-    nk, nv = to_dev(w.new_k, w.spec.kv_dtype), to_dev(w.new_v, w.spec.kv_dtype)
-    slots = torch.from_numpy(w.new_slots).cuda()
-    ms = time_calls(lambda: abi.kv_cache_write(nk, nv, slots, k, v), 50)
-    rows["kv_slot_write"] = {"us": round(ms * 1e3, 2), "bound": "latency",
-                             "workload": f"{SECONDARY}: 32 new tokens x 2 kv heads x 128, f16"}
+    if want("kv_slot_write"):
+        w = workloads.generate(SECONDARY)
+        k, v, _ = gpu_pool(w, with_new_tokens=False)
+        nk, nv = to_dev(w.new_k, w.spec.kv_dtype), to_dev(w.new_v, w.spec.kv_dtype)
+        slots = torch.from_numpy(w.new_slots).cuda()
+        ms = time_calls(lambda: abi.kv_cache_write(nk, nv, slots, k, v), 50)
+        rows["kv_slot_write"] = {"us": round(ms * 1e3, 2), "bound": "latency",
+                                 "workload": f"{SECONDARY}: 32 new tokens x 2 kv heads x 128, f16"}
     return rows
 
 
@@ -384,6 +402,9 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="layer pools rotated through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="profiling aid: run only these comma-separated rows (" + ", ".join(ROW_NAMES) +
+                         ") and print {\"rows\": ...}; no headline line")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other rows of the path (FP8, window, multi-token, quantise, append, copy, write)")
     ap.add_argument("--path", choices=["pair", "fused", "balanced"], default="pair",
@@ -405,6 +426,14 @@ def main():
 
     torch.cuda.set_device(0)
     digest = source_digest()
+    if args.only:
+        only = [x for x in args.only.split(",") if x]
+        bad = [x for x in only if x not in ROW_NAMES]
+        if bad:
+            print(f"unknown rows {bad}; rows are {list(ROW_NAMES)}", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"rows": measure_rows(args, only), "kernel_source_digest": digest}), flush=True)
+        return
     if args.copy_calibration:
         a = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         torch.empty_like(a).copy_(a)

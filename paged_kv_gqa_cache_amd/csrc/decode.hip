@@ -381,7 +381,7 @@ struct WaveState {
 // lane's head column also masks positions after its own limit lim) through
 // one wave's softmax state.  `ids` holds the
 // physical ids of the first 64 of them (lane j: block first + stride*j).
-template <int KVT, int D, int PF, bool CAUSAL = false>
+template <int KVT, int D, int PF, bool CAUSAL = false, int POLICY = CAUSAL ? 0 : kStreamLoad>
 __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int h, int L, int lo, int first,
                                               int stride, int count, int ids,
                                               const u32x4 (&qop)[TileOps<KVT, D>::NQ],
@@ -406,10 +406,9 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int 
   // A load past the last block still issues, through a zero-size
   // descriptor (reads 0, no memory traffic), so the loop has no
   // conditional loads and each wait covers exactly the tile it needs.
-  // A decode step reads each K/V tile once, so its loads are non-temporal.
-  // In the multi-token step (CAUSAL) every pack of a sequence's query rows
-  // reads the same tiles again, so they stay ordinary, cacheable loads.
-  constexpr int kTilePolicy = CAUSAL ? 0 : kStreamLoad;
+  // POLICY: cache policy of the tile loads, kStreamLoad (non-temporal) for
+  // tiles one step reads once, 0 (ordinary) for tiles other work reads
+  // again soon (the multi-token step's, read by every pack of query rows).
   // E4M3: the block's K and V scales ride in the ring with its tile, loaded
   // just before the tile's codes, so the wait for a tile covers its scales
   // and never the tiles prefetched after it.
@@ -425,9 +424,9 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int 
     const auto kr = make_tile_rsrc(kcache + tile, valid ? TILE : 0);
     const auto vr = make_tile_rsrc(vcache + tile, valid ? TILE : 0);
 #pragma unroll
-    for (int m = 0; m < NL; ++m) kt[m] = buffer_ld16_policy<kTilePolicy>(kr, lane_off[m]);
+    for (int m = 0; m < NL; ++m) kt[m] = buffer_ld16_policy<POLICY>(kr, lane_off[m]);
 #pragma unroll
-    for (int m = 0; m < NL; ++m) vt[m] = buffer_ld16_policy<kTilePolicy>(vr, lane_off[m]);
+    for (int m = 0; m < NL; ++m) vt[m] = buffer_ld16_policy<POLICY>(vr, lane_off[m]);
   };
 
   auto process = [&](const u32x4 (&kt)[NL], u32x4 (&vt)[NL], float ksc, float vsc, int i) {
@@ -587,7 +586,14 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
   const int nmine = first < blk1 ? (blk1 - first + NW - 1) / NW : 0;
   WaveState<NT> st;
   st.reset();
-  attend_blocks<KVT, D, PF>(p, b, h, L, lo, first, NW, nmine, pf.ids, pf.qop, st);
+  // Tile loads stream (non-temporal) except in a split sequence's first
+  // partition: prompts shared between sequences (parallel samples, beams, a
+  // common system prompt) sit at the start, and the sequences sharing them
+  // read those tiles close in time, so there they stay cacheable.
+  if (MODE != MODE_FINAL && part == 0)
+    attend_blocks<KVT, D, PF, false, 0>(p, b, h, L, lo, first, NW, nmine, pf.ids, pf.qop, st);
+  else
+    attend_blocks<KVT, D, PF, false, kStreamLoad>(p, b, h, L, lo, first, NW, nmine, pf.ids, pf.qop, st);
   float m_run = st.m;
   float l_run = st.l;
   f32x4 (&o)[NT] = st.o;
