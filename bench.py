@@ -247,6 +247,56 @@ def hbm_row(bytes_per_call: int, ms: float, what: str) -> dict:
             "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes": bytes_per_call, "bytes_are": what}
 
 
+def torch_materialising(r, steps: int) -> dict:
+    """The headline decode step in plain PyTorch on the GPU, for context (the
+    comparison "LLM Serving Kernels", section "Verified NVIDIA L4 release",
+    makes against a materialising PyTorch reference): every sequence's K/V
+    is gathered out of the paged pool into dense, zero-padded fp32 tensors
+    (the tile layout undone by an index), then matmul, masked softmax,
+    matmul.  Layer pools rotate as in the timed steps.  Not part of the path."""
+    import torch
+    s = r.spec
+    B, Hq, Hkv, D = s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim
+    G = Hq // Hkv
+    e = {"f32": 4, "f16": 2, "bf16": 2}[s.kv_dtype]
+    x, nn = 16 // e, 4 // e
+    t = torch.arange(16).view(16, 1)
+    d = torch.arange(D).view(1, D)
+    # tile position of (token slot t, dim d), as the cache layout defines it
+    pk = (((d // x) * 16 + t) * x + d % x).reshape(-1).cuda()
+    pv = (((((d // (16 * nn)) * 4 + t // 4) * 16 + d % 16) * nn + (d // 16) % nn) * 4 + t % 4).reshape(-1).cuda()
+    mbps = r.tables.shape[1]
+    T = mbps * 16
+    idx = r.tables.long().clamp(min=0)
+    keep = torch.arange(T, device="cuda")[None, :] < r.lens.long()[:, None]
+    q = r.q.float().view(B, Hkv, G, D)
+
+    def step(i):
+        k, v, _ = r.pools[i % len(r.pools)]
+        K = k[idx][..., pk].view(B, mbps, Hkv, 16, D).permute(0, 2, 1, 3, 4).reshape(B, Hkv, T, D).float()
+        V = v[idx][..., pv].view(B, mbps, Hkv, 16, D).permute(0, 2, 1, 3, 4).reshape(B, Hkv, T, D).float()
+        V = V.masked_fill(~keep[:, None, :, None], 0.0)   # slots past the context hold no data
+        S = torch.matmul(q, K.transpose(-1, -2).contiguous()) * r.w.scale
+        S = S.masked_fill(~keep[:, None, None, :], float("-inf"))
+        return torch.matmul(torch.softmax(S, dim=-1), V.contiguous()).reshape(B, Hq, D)
+
+    # agreement with the path on one layer (outside the timing)
+    k, v, sc = r.pools[0]
+    from paged_kv_gqa_cache_amd import abi
+    ours = abi.paged_decode_attention(r.q, k, v, r.tables, r.lens, r.w.scale, sc, out_dtype=torch.float32)
+    diff = float((step(0) - ours).abs().max())
+    it = [0]
+
+    def call():
+        step(it[0])
+        it[0] += 1
+
+    ms = time_calls(call, steps, warmup=2)
+    return {"us": round(ms * 1e3, 1), "max_abs_diff_vs_path": diff,
+            "what": "plain PyTorch on the GPU: gather to dense zero-padded fp32 K/V, matmul, masked softmax, "
+                    "matmul (context for the materialising-reference comparison; not part of the path)"}
+
+
 ROW_NAMES = ("fp8_e4m3_decode", "e4m3_bulk_quantise", "e4m3_append", "sliding_window", "chunked_prefill",
              "spec_verify_4", "copy_blocks", "kv_slot_write")
 
@@ -402,6 +452,8 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="layer pools rotated through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-torch-reference", action="store_true",
+                    help="skip timing the materialising PyTorch reference of the headline step")
     ap.add_argument("--only", default=None,
                     help="profiling aid: run only these comma-separated rows (" + ", ".join(ROW_NAMES) +
                          ") and print {\"rows\": ...}; no headline line")
@@ -458,6 +510,12 @@ def main():
                "seqs_layers_per_s": round(r2.spec.num_seqs / t2, 1)}
         del r2
 
+    torch_ref = None
+    if not args.no_torch_reference:
+        torch_ref = torch_materialising(r, 10)
+        torch_ref["path_us_per_step"] = round(t_step * 1e6, 2)
+        torch_ref["path_speedup"] = round(torch_ref["us"] / (t_step * 1e6), 1)
+
     rows = None
     if not args.no_rows and args.workload == HEADLINE:
         rows = measure_rows(args)
@@ -498,6 +556,7 @@ def main():
         },
         "b32": b32,
         "rows": rows,
+        "torch_materialising": torch_ref,
         "kernel_source_digest": digest,
         "library": abi.version(),
     }
