@@ -364,7 +364,7 @@ def measure_rows(args, only=None) -> dict:
     # Multi-token step: chunked prefill (1-256 new tokens per sequence) and
     # speculative verification (4 tokens per sequence).
     for key, kw, P in (("chunked_prefill", {}, 1024),
-                       ("spec_verify_4", dict(num_seqs=64, query_tokens=("uniform", 4, 4)), 512)):
+                       ("spec_verify_4", dict(num_seqs=64, query_tokens=("uniform", 4, 4)), 0)):
         if not want(key):
             continue
         w = workloads.generate("qwen25_7b_chunk", **kw)

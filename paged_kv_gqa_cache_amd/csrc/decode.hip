@@ -41,6 +41,7 @@
 #include "pkv_launch.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace pkv {
 
@@ -1225,19 +1226,25 @@ constexpr int ring_depth() {
   return kPrefetch;
 }
 
-// Workgroups of `kernel` that fit on the current device at once (compute
-// units x resident workgroups per unit); queried once per kernel and device.
-template <typename K>
-static int resident_workgroups(K kernel, int block) {
-  static int cached[16] = {0};
+// Workgroups of kernel KERNEL that fit on the current device at once
+// (compute units x resident workgroups per unit); queried once per kernel
+// and device.  The kernel is a template argument so that every kernel has a
+// cache of its own (they share one function type).
+template <auto KERNEL, int MAX_PER_CU = 0>
+static int resident_workgroups(int block) {
+  static std::atomic<int> cached[16];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  if (dev < 16 && cached[dev] > 0) return cached[dev];
+  if (dev < 16) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu <= 0) per_cu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERNEL, block, 0) != hipSuccess || per_cu <= 0) per_cu = 1;
+  if (MAX_PER_CU > 0) per_cu = std::min(per_cu, MAX_PER_CU);
   const int n = cus * per_cu;
-  if (dev < 16) cached[dev] = n;
+  if (dev < 16) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -1249,7 +1256,7 @@ static hipError_t launch_mode(const DecodeParams& p, hipStream_t stream) {
   if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   if (p.num_seqs <= kMaxSeqsPersistent) {
     auto kernel = paged_decode_persistent<KVT, D, kWaves, MODE, PF>;
-    int64_t grid = std::min<int64_t>(items, resident_workgroups(kernel, block));
+    int64_t grid = std::min<int64_t>(items, resident_workgroups<paged_decode_persistent<KVT, D, kWaves, MODE, PF>>(block));
     grid = std::max<int64_t>(kXcds, grid / kXcds * kXcds);
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(block), 0, stream, p);
   } else {
@@ -1272,7 +1279,10 @@ static hipError_t launch_decode_t(DecodeParams p, int mode, hipStream_t stream) 
 template <int KVT, int D>
 static int stream_grid() {
   constexpr int kPf = ring_depth<KVT, D>();
-  const int res = resident_workgroups(paged_decode_stream<KVT, D, kWaves, kPf>, kWaves * 64);
+  // At most two workgroups per CU: where registers allow three (the 16-bit
+  // and E4M3 kernels), the third made the FP8 layer 6% and the ragged B=128
+  // layer 4% slower (smaller shares, more segments to merge).
+  const int res = resident_workgroups<paged_decode_stream<KVT, D, kWaves, kPf>, 2>(kWaves * 64);
   return std::max(kXcds, res / kXcds * kXcds);
 }
 
@@ -1335,7 +1345,7 @@ template <int KVT, int D, int MODE>
 static hipError_t launch_prefill_t(const DecodeParams& p, hipStream_t stream) {
   constexpr int kPf = ring_depth<KVT, D>();
   auto kernel = paged_prefill_persistent<KVT, D, kWaves, MODE, kPf>;
-  const int grid = std::max(kXcds, resident_workgroups(kernel, kWaves * 64) / kXcds * kXcds);
+  const int grid = std::max(kXcds, resident_workgroups<paged_prefill_persistent<KVT, D, kWaves, MODE, kPf>>(kWaves * 64) / kXcds * kXcds);
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
