@@ -382,11 +382,15 @@ struct WaveState {
 // lane's head column also masks positions after its own limit lim) through
 // one wave's softmax state.  `ids` holds the
 // physical ids of the first 64 of them (lane j: block first + stride*j).
-template <int KVT, int D, int PF, bool CAUSAL = false, int POLICY = CAUSAL ? 0 : kStreamLoad>
-__device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int h, int L, int lo, int first,
-                                              int stride, int count, int ids,
-                                              const u32x4 (&qop)[TileOps<KVT, D>::NQ],
-                                              WaveState<D / 16>& st, int lim = 0) {
+//
+// NPK > 1 (the multi-token step): NPK packs of query columns share every
+// tile, each with its own q operand, softmax state and causal limits, so a
+// tile fetched once serves NPK x 16 columns.
+template <int KVT, int D, int PF, bool CAUSAL, int POLICY, int NPK>
+__device__ __forceinline__ void attend_packs(const DecodeParams& p, int b, int h, int L, int lo, int first,
+                                             int stride, int count, int ids,
+                                             const u32x4 (&qop)[NPK][TileOps<KVT, D>::NQ],
+                                             WaveState<D / 16> (&st)[NPK], const int (&lim)[NPK]) {
   typedef TileOps<KVT, D> T;
   constexpr int E = ElemBytes<KVT>::value;
   constexpr int TILE = kBlockSize * D * E;  // bytes of one (block, kv head) tile
@@ -430,52 +434,67 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int 
     for (int m = 0; m < NL; ++m) vt[m] = buffer_ld16_policy<POLICY>(vr, lane_off[m]);
   };
 
+  // Lowest causal limit of each pack (wave-uniform: lane 0 holds the pack's
+  // first token, the smallest limit); blocks that end at or before it need
+  // no causal mask.
+  int lim_lo[NPK];
+#pragma unroll
+  for (int k = 0; k < NPK; ++k) lim_lo[k] = CAUSAL ? __builtin_amdgcn_readfirstlane(lim[k]) : 0;
+
   auto process = [&](const u32x4 (&kt)[NL], u32x4 (&vt)[NL], float ksc, float vsc, int i) {
     const int tok0 = (first + stride * i) * kBlockSize;
-    const f32x4 s = T::qk(kt, qop);
     float f = p.qk_scale_log2;
     float pscale = 1.f;
     if constexpr (KVT == KV_E4M3) {
       f *= ksc;
       pscale = 256.f * vsc;
     }
-    float x[4];
+    const bool tail = tok0 + kBlockSize > L;   // the sequence's last, partly filled block
+    if (tail) T::mask_v(vt, L - tok0 - 4 * g);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = s[j] * f;
-    if (tok0 + kBlockSize > L) {  // the sequence's last, partly filled block
-      const int nv = L - tok0 - 4 * g;
+    for (int k = 0; k < NPK; ++k) {
+      const f32x4 s = T::qk(kt, qop[k]);
+      float x[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = (j < nv) ? x[j] : -INFINITY;
-      T::mask_v(vt, nv);
+      for (int j = 0; j < 4; ++j) x[j] = s[j] * f;
+      if (tail) {
+        const int nv = L - tok0 - 4 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = (j < nv) ? x[j] : -INFINITY;
+      }
+      if (tok0 < lo) {              // the window's first block: positions before lo
+        const int nlo = lo - tok0 - 4 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = (j < nlo) ? -INFINITY : x[j];
+      }
+      if constexpr (CAUSAL) {       // this lane's column sees positions <= lim only
+        if (tok0 + kBlockSize - 1 > lim_lo[k]) {
+          const int nc = lim[k] - tok0 - 4 * g;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[j] = (j <= nc) ? x[j] : -INFINITY;
+        }
+      }
+      // Lazy rescaling: the reference max only moves when some head's block
+      // max exceeds it by more than kSlack (log2 units), so exp2(x - m)
+      // stays below 2^kSlack and the accumulators are rescaled about once
+      // per run of blocks instead of every block.  The first block always
+      // moves it.
+      WaveState<NT>& sk = st[k];
+      const float bm = max_over_groups(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      if (__any(bm > sk.m + kSlack)) {
+        const float m_new = fmaxf(sk.m, bm);
+        const float alpha = fast_exp2(sk.m - m_new);
+        sk.m = m_new;
+        sk.l *= alpha;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) sk.o[n] *= alpha;
+      }
+      float pr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - sk.m);
+      sk.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      T::pv(sk.o, vt, pr, pscale);
     }
-    if (tok0 < lo) {              // the window's first block: positions before lo
-      const int nlo = lo - tok0 - 4 * g;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = (j < nlo) ? -INFINITY : x[j];
-    }
-    if constexpr (CAUSAL) {       // this lane's column sees positions <= lim only
-      const int nc = lim - tok0 - 4 * g;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = (j <= nc) ? x[j] : -INFINITY;
-    }
-    // Lazy rescaling: the reference max only moves when some head's block
-    // max exceeds it by more than kSlack (log2 units), so exp2(x - m) stays
-    // below 2^kSlack and the accumulators are rescaled about once per run
-    // of blocks instead of every block.  The first block always moves it.
-    const float bm = max_over_groups(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-    if (__any(bm > st.m + kSlack)) {
-      const float m_new = fmaxf(st.m, bm);
-      const float alpha = fast_exp2(st.m - m_new);
-      st.m = m_new;
-      st.l *= alpha;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) st.o[n] *= alpha;
-    }
-    float pr[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - st.m);
-    st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    T::pv(st.o, vt, pr, pscale);
   };
 
   // Blocks go in chunks of up to 64: the chunk's physical ids arrive in one
@@ -505,8 +524,24 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int 
   }
   if constexpr (KVT == KV_E4M3) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) st.o[n] *= T::kOutScale;
+    for (int k = 0; k < NPK; ++k)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) st[k].o[n] *= T::kOutScale;
   }
+}
+
+// One pack of query columns (decode: the GQA group of one token).
+template <int KVT, int D, int PF, bool CAUSAL = false, int POLICY = CAUSAL ? 0 : kStreamLoad>
+__device__ __forceinline__ void attend_blocks(const DecodeParams& p, int b, int h, int L, int lo, int first,
+                                              int stride, int count, int ids,
+                                              const u32x4 (&qop)[TileOps<KVT, D>::NQ],
+                                              WaveState<D / 16>& st, int lim = 0) {
+  WaveState<D / 16> sa[1] = {st};
+  const int la[1] = {lim};
+  attend_packs<KVT, D, PF, CAUSAL, POLICY, 1>(
+      p, b, h, L, lo, first, stride, count, ids,
+      *reinterpret_cast<const u32x4(*)[1][TileOps<KVT, D>::NQ]>(&qop), sa, la);
+  st = sa[0];
 }
 
 // Merges the NW waves' softmax states of one item through LDS: M and Lsum
@@ -805,41 +840,59 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_persistent(const DecodeP
 // token j attends causally to positions 0 .. L - n_b + j ("rvLLM:
 // High-performance LLM inference in Rust", section "CUDA Kernels", row
 // "FlashAttention-2": prefill and decode with causal masking).  A pack of
-// TP = 16 / G tokens x G heads fills the 16 matrix-core columns, so each K/V
-// tile fetched serves TP tokens of the whole group, and each column masks the
-// positions after its own token.  Work items are (sequence, kv head, pack,
-// partition); a pack's partitions cover the blocks up to its last token.
+// TP = 16 / G tokens x G heads fills the 16 matrix-core columns, and each
+// column masks the positions after its own token.  A wave carries
+// kPacksPerWave packs at once, so each K/V tile it fetches serves
+// kPacksPerWave x TP tokens of the whole group.  Work items are (sequence,
+// kv head, group of packs, partition); a group's partitions cover the
+// blocks up to its last token.
+constexpr int kPacksPerWave = 2;
 struct QueryRows {
   int q0;   // first query row of the sequence
   int n;    // its number of query rows (<= its context length)
 };
 
-template <int KVT, int D, int NW>
-__device__ __forceinline__ void prefill_prefetch(const DecodeParams& p, int b, int h, int pack, int part,
-                                                 QueryRows qrow, ItemPrefetch<KVT, D>& pf) {
+// A work item's loads that do not depend on its math, for NPK packs: the
+// wave's first 64 block ids and each pack's q operand.
+template <int KVT, int D, int NPK>
+struct PackPrefetch {
+  int ids;
+  u32x4 qop[NPK][TileOps<KVT, D>::NQ];
+};
+
+template <int KVT, int D, int NW, int NPK>
+__device__ __forceinline__ void prefill_prefetch(const DecodeParams& p, int b, int h, int grp, int part,
+                                                 QueryRows qrow, PackPrefetch<KVT, D, NPK>& pf) {
   constexpr int QB = (KVT == KV_F32) ? 4 : 2;
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
   const int G = p.group;
-  const int j0 = pack * p.tokens_per_pack;
-  const int ncols = min(p.tokens_per_pack, qrow.n - j0) * G;
   const auto tr = make_tile_rsrc(p.block_tables + static_cast<size_t>(b) * p.mbps, p.mbps * 4);
   const int id0 = part * p.partition_blocks + wid + NW * lane;
   pf.ids = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(tr, static_cast<uint32_t>(id0) * 4u, 0, 0));
   const uint32_t row_bytes = static_cast<uint32_t>(p.num_q_heads * D * QB);
   const auto qr = make_tile_rsrc(static_cast<const char*>(p.q) + static_cast<size_t>(qrow.q0) * row_bytes,
                                  qrow.n * row_bytes);
-  // Column r: token j0 + r / G, head h * G + r % G; unused columns read
-  // past the descriptor's end, i.e. zeros.
-  const uint32_t qoff = r < ncols ? static_cast<uint32_t>(((j0 + r / G) * p.num_q_heads + h * G + r % G) * D * QB)
-                                  : static_cast<uint32_t>(qrow.n) * row_bytes;
-  TileOps<KVT, D>::load_q(pf.qop, qr, qoff, lane >> 4);
+#pragma unroll
+  for (int k = 0; k < NPK; ++k) {
+    // Column r of pack k: token j0 + r / G, head h * G + r % G; unused
+    // columns (and packs past the sequence's rows) read past the
+    // descriptor's end, i.e. zeros.
+    const int j0 = (grp * NPK + k) * p.tokens_per_pack;
+    const int ncols = max(0, min(p.tokens_per_pack, qrow.n - j0)) * G;
+    const uint32_t qoff = r < ncols ? static_cast<uint32_t>(((j0 + r / G) * p.num_q_heads + h * G + r % G) * D * QB)
+                                    : static_cast<uint32_t>(qrow.n) * row_bytes;
+    TileOps<KVT, D>::load_q(pf.qop[k], qr, qoff, lane >> 4);
+  }
 }
 
-template <int KVT, int D, int NW, int MODE, int PF>
-__device__ __forceinline__ void prefill_item(const DecodeParams& p, int b, int h, int pack, int part, int L,
-                                             QueryRows qrow, const ItemPrefetch<KVT, D>& pf,
+// One work item: sequence b, kv head h, packs grp*NPK .. grp*NPK + NPK - 1
+// (TP = tokens_per_pack tokens each), partition `part` of the blocks up to
+// the group's last token.
+template <int KVT, int D, int NW, int MODE, int PF, int NPK>
+__device__ __forceinline__ void prefill_item(const DecodeParams& p, int b, int h, int grp, int part, int L,
+                                             QueryRows qrow, const PackPrefetch<KVT, D, NPK>& pf,
                                              ItemShared<NW, D / 16>& sm) {
   constexpr int NT = D / 16;
   const int lane = threadIdx.x & 63;
@@ -847,40 +900,54 @@ __device__ __forceinline__ void prefill_item(const DecodeParams& p, int b, int h
   const int g = lane >> 4;
   const int r = lane & 15;
   const int G = p.group;
-  const int j0 = pack * p.tokens_per_pack;
-  const int ntok = min(p.tokens_per_pack, qrow.n - j0);
-  const bool valid = r < ntok * G;
-  const int jj = valid ? r / G : ntok - 1;
-  const int pos = L - qrow.n + j0 + jj;             // last position this column sees
-  const int l_item = L - qrow.n + j0 + ntok;        // positions the pack reads
+  const int TP = p.tokens_per_pack;
+  const int base = L - qrow.n;                      // position of the sequence's first query row
+  int pos[NPK];                                     // last position each column sees (-1: none)
+  int jj[NPK];
+  bool valid[NPK];
+#pragma unroll
+  for (int k = 0; k < NPK; ++k) {
+    const int j0 = (grp * NPK + k) * TP;
+    const int ntok = max(0, min(TP, qrow.n - j0));
+    valid[k] = r < ntok * G;
+    jj[k] = valid[k] ? r / G : 0;
+    pos[k] = valid[k] ? base + j0 + jj[k] : -1;
+  }
+  const int l_item = base + min(qrow.n, (grp + 1) * NPK * TP);   // positions the group reads
   const int nblk = (l_item + kBlockSize - 1) / kBlockSize;
   const int blk0 = part * p.partition_blocks;
   if (blk0 >= nblk) return;
   const int blk1 = min(nblk, blk0 + p.partition_blocks);
   const int first = blk0 + wid;
   const int nmine = first < blk1 ? (blk1 - first + NW - 1) / NW : 0;
-  WaveState<NT> st;
-  st.reset(-1e30f);   // finite: a column may see no position in a wave's blocks
-  attend_blocks<KVT, D, PF, true>(p, b, h, l_item, 0, first, NW, nmine, pf.ids, pf.qop, st, pos);
-  const float l_run = sum_over_groups(st.l);
+  WaveState<NT> st[NPK];
+#pragma unroll
+  for (int k = 0; k < NPK; ++k) st[k].reset(-1e30f);   // finite: a column may see no position in a wave's blocks
+  attend_packs<KVT, D, PF, true, 0, NPK>(p, b, h, l_item, 0, first, NW, nmine, pf.ids, pf.qop, st, pos);
 
-  const size_t row = static_cast<size_t>(qrow.q0 + j0 + jj) * p.num_q_heads + h * G + r % G;
-  const bool col_ok = valid && blk0 * kBlockSize <= pos;   // the partition holds a position of the column
-  auto emit = [&](int n, f32x4 acc) {
-    if (!col_ok) return;
-    if (MODE == MODE_FINAL) store4(p.out, row * D + 16 * n + 4 * g, p.out_dtype, acc);
-    else *reinterpret_cast<f32x4*>(p.tmp_out + (row * p.num_partitions + part) * D + 16 * n + 4 * g) = acc;
-  };
-  float M, Lsum;
-  merge_waves<NW, NT>(st.m, l_run, st.o, sm, wid, lane, M, Lsum, emit);
-  if (MODE == MODE_PARTIAL && wid == 0 && g == 0 && col_ok)
-    p.tmp_lse[row * p.num_partitions + part] = (M + fast_log2(Lsum)) * kLn2;
+#pragma unroll
+  for (int k = 0; k < NPK; ++k) {
+    const float l_run = sum_over_groups(st[k].l);
+    const int j0 = (grp * NPK + k) * TP;
+    const size_t row = static_cast<size_t>(qrow.q0 + j0 + jj[k]) * p.num_q_heads + h * G + r % G;
+    const bool col_ok = valid[k] && blk0 * kBlockSize <= pos[k];   // the partition holds a position of it
+    auto emit = [&](int n, f32x4 acc) {
+      if (!col_ok) return;
+      if (MODE == MODE_FINAL) store4(p.out, row * D + 16 * n + 4 * g, p.out_dtype, acc);
+      else *reinterpret_cast<f32x4*>(p.tmp_out + (row * p.num_partitions + part) * D + 16 * n + 4 * g) = acc;
+    };
+    if (k > 0) __syncthreads();   // the previous pack's merge has read the shared state
+    float M, Lsum;
+    merge_waves<NW, NT>(st[k].m, l_run, st[k].o, sm, wid, lane, M, Lsum, emit);
+    if (MODE == MODE_PARTIAL && wid == 0 && g == 0 && col_ok)
+      p.tmp_lse[row * p.num_partitions + part] = (M + fast_log2(Lsum)) * kLn2;
+  }
 }
 
 // Persistent form of the multi-token step, laid out like
 // paged_decode_persistent: LDS prefix sums of each sequence's items, XCD
 // ranges, the next item's ids and q prefetched during the current one.
-template <int KVT, int D, int NW, int MODE, int PF>
+template <int KVT, int D, int NW, int MODE, int PF, int NPK>
 __global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const DecodeParams p) {
   __shared__ ItemShared<NW, D / 16> sm;
   __shared__ int s_cum[kMaxSeqsPersistent + 1];   // items before sequence b
@@ -892,8 +959,8 @@ __global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const Decode
   const int wid = threadIdx.x >> 6;
   const int B = p.num_seqs;
   const int Hkv = p.num_kv_heads;
-  const int TP = p.tokens_per_pack;
-  auto parts_of = [&](int L, int n) {   // partitions of each pack of a sequence
+  const int TPG = p.tokens_per_pack * NPK;   // tokens of a group of packs
+  auto parts_of = [&](int L, int n) {   // partitions of each group of a sequence
     return n > 0 ? ((L + kBlockSize - 1) / kBlockSize + p.partition_blocks - 1) / p.partition_blocks : 0;
   };
 
@@ -909,7 +976,7 @@ __global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const Decode
       s_len[i] = L;
       s_q0[i] = q0;
       s_nq[i] = n;
-      items = Hkv * ((n + TP - 1) / TP) * parts_of(L, n);
+      items = Hkv * ((n + TPG - 1) / TPG) * parts_of(L, n);
     }
     int x = items;
 #pragma unroll
@@ -933,7 +1000,7 @@ __global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const Decode
   const int per_xcd = gridDim.x / kXcds;
   const int lo = static_cast<int>(static_cast<int64_t>(N) * xcd / kXcds);
   const int hi = static_cast<int>(static_cast<int64_t>(N) * (xcd + 1) / kXcds);
-  // Item n -> (sequence, kv head, pack, partition), partition fastest.
+  // Item n -> (sequence, kv head, group of packs, partition), partition fastest.
   auto locate = [&](int n, int& b, int& h, int& pack, int& part) {
     int lo_b = 0, hi_b = B;
     while (hi_b - lo_b > 1) {
@@ -943,7 +1010,7 @@ __global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const Decode
     }
     b = lo_b;
     const int parts = parts_of(s_len[b], s_nq[b]);
-    const int per_head = ((s_nq[b] + TP - 1) / TP) * parts;
+    const int per_head = ((s_nq[b] + TPG - 1) / TPG) * parts;
     const int local = n - s_cum[b];
     h = local / per_head;
     const int rem = local % per_head;
@@ -953,14 +1020,14 @@ __global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const Decode
   int n = lo + static_cast<int>(blockIdx.x) / kXcds;
   if (n >= hi) return;
   int b, h, pack, part, b2, h2, pack2, part2;
-  ItemPrefetch<KVT, D> cur, nxt;
+  PackPrefetch<KVT, D, NPK> cur, nxt;
   locate(n, b, h, pack, part);
-  prefill_prefetch<KVT, D, NW>(p, b, h, pack, part, QueryRows{s_q0[b], s_nq[b]}, cur);
+  prefill_prefetch<KVT, D, NW, NPK>(p, b, h, pack, part, QueryRows{s_q0[b], s_nq[b]}, cur);
   while (true) {
     const int n2 = n + per_xcd;
     locate(min(n2, hi - 1), b2, h2, pack2, part2);
-    prefill_prefetch<KVT, D, NW>(p, b2, h2, pack2, part2, QueryRows{s_q0[b2], s_nq[b2]}, nxt);
-    prefill_item<KVT, D, NW, MODE, PF>(p, b, h, pack, part, s_len[b], QueryRows{s_q0[b], s_nq[b]}, cur, sm);
+    prefill_prefetch<KVT, D, NW, NPK>(p, b2, h2, pack2, part2, QueryRows{s_q0[b2], s_nq[b2]}, nxt);
+    prefill_item<KVT, D, NW, MODE, PF, NPK>(p, b, h, pack, part, s_len[b], QueryRows{s_q0[b], s_nq[b]}, cur, sm);
     __syncthreads();   // the next item reuses the merge state
     if (n2 >= hi) break;
     n = n2;
@@ -1344,8 +1411,11 @@ hipError_t launch_stream_merge(const ReduceParams& p, hipStream_t stream) {
 template <int KVT, int D, int MODE>
 static hipError_t launch_prefill_t(const DecodeParams& p, hipStream_t stream) {
   constexpr int kPf = ring_depth<KVT, D>();
-  auto kernel = paged_prefill_persistent<KVT, D, kWaves, MODE, kPf>;
-  const int grid = std::max(kXcds, resident_workgroups<paged_prefill_persistent<KVT, D, kWaves, MODE, kPf>>(kWaves * 64) / kXcds * kXcds);
+#ifndef PKV_PACKS
+#define PKV_PACKS kPacksPerWave
+#endif
+  constexpr auto kernel = paged_prefill_persistent<KVT, D, kWaves, MODE, kPf, PKV_PACKS>;
+  const int grid = std::max(kXcds, resident_workgroups<kernel>(kWaves * 64) / kXcds * kXcds);
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }

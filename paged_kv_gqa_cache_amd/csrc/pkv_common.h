@@ -68,14 +68,42 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Max / sum over the four lanes that share lane % 16 (lanes r, r+16, r+32, r+48).
+// Max / sum over the four lanes that share lane % 16 (lanes r, r+16, r+32,
+// r+48), with gfx950's lane swaps (VALU, no LDS round trip): with both
+// operands x, v_permlane16_swap returns (rows 0,0,2,2 ; rows 1,1,3,3) of x
+// and v_permlane32_swap (lanes 0-31 twice ; lanes 32-63 twice), so the two
+// results hold every lane's partner across 16 (then 32).  The partner sums
+// pair the same values as x + shuffle-xor would, so the bits match.
+// The second operand goes through an opaque copy: given one value for both,
+// the compiler takes the two results as equal and drops the combine.
+__device__ __forceinline__ uint32_t opaque_copy(uint32_t x) {
+  uint32_t y;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+  return y;
+}
+template <bool ROWS16>
+__device__ __forceinline__ void lane_swap(float x, float& lo_half, float& hi_half) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = ROWS16 ? __builtin_amdgcn_permlane16_swap(u, opaque_copy(u), false, false)
+                        : __builtin_amdgcn_permlane32_swap(u, opaque_copy(u), false, false);
+  lo_half = __uint_as_float(r[0]);   // the lower of the two partner lanes' values
+  hi_half = __uint_as_float(r[1]);   // the upper one's
+}
 __device__ __forceinline__ float max_over_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  float a, b;
+  lane_swap<true>(x, a, b);
+  x = fmaxf(a, b);
+  lane_swap<false>(x, a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float sum_over_groups(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  // (x_l + x_(l^16)) + (x_(l^32) + x_(l^48)), as the shuffle form; IEEE
+  // addition is commutative, so which operand is the lane's own is moot
+  float a, b;
+  lane_swap<true>(x, a, b);
+  x = a + b;
+  lane_swap<false>(x, a, b);
+  return a + b;
 }
 
 // ------------------------------------------------------------ matrix cores
