@@ -1411,10 +1411,7 @@ hipError_t launch_stream_merge(const ReduceParams& p, hipStream_t stream) {
 template <int KVT, int D, int MODE>
 static hipError_t launch_prefill_t(const DecodeParams& p, hipStream_t stream) {
   constexpr int kPf = ring_depth<KVT, D>();
-#ifndef PKV_PACKS
-#define PKV_PACKS kPacksPerWave
-#endif
-  constexpr auto kernel = paged_prefill_persistent<KVT, D, kWaves, MODE, kPf, PKV_PACKS>;
+  constexpr auto kernel = paged_prefill_persistent<KVT, D, kWaves, MODE, kPf, kPacksPerWave>;
   const int grid = std::max(kXcds, resident_workgroups<kernel>(kWaves * 64) / kXcds * kXcds);
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
