@@ -591,6 +591,19 @@ def test_prefill_matches_oracle(kw, P):
     assert max_err(_prefill_gpu(w, gpu_pool(w), P), _prefill_oracle(w)) <= TOL
 
 
+@pytest.mark.parametrize("P", [0, 64])
+@pytest.mark.parametrize("kw", [dict(), dict(num_q_heads=32, num_kv_heads=2)])
+def test_prefill_partial_pack_groups(kw, P):
+    """1-9 new tokens per sequence: a wave carries two packs, so groups whose
+    second pack is empty or partly filled (G = 7: 2 tokens per pack; G = 16:
+    1) must still match the oracle row by row."""
+    _announce("prefill partial groups", kw, P)
+    w = workloads.generate("qwen25_7b_chunk", num_seqs=12, lengths=("uniform", 9, 500),
+                           query_tokens=("uniform", 1, 9), **kw)
+    assert set(np.diff(w.query_start).tolist()) >= {1, 2, 3}
+    assert max_err(_prefill_gpu(w, gpu_pool(w), P), _prefill_oracle(w)) <= TOL
+
+
 def test_prefill_with_one_new_token_is_decode_bitwise():
     _announce("prefill n=1")
     from paged_kv_gqa_cache_amd import abi
@@ -620,13 +633,14 @@ def test_prefill_whole_context_new_and_16bit_output():
 
 
 def test_prefill_full_size_sampled():
-    """The 16-sequence chunked-prefill workload at full size (in the
-    partitioned configuration), checked on three sequences' rows."""
+    """The 16-sequence chunked-prefill workload at full size, in one pass (the
+    benchmarked configuration) and partitioned, checked on three sequences'
+    rows."""
     _announce("prefill full size")
     w = workloads.generate("qwen25_7b_chunk")
     pool = gpu_pool(w)
-    got = _prefill_gpu(w, pool, 512).cpu().numpy()
-    assert np.all(np.isfinite(got))
+    runs = [_prefill_gpu(w, pool, P).cpu().numpy() for P in (0, 512)]
+    assert all(np.all(np.isfinite(g)) for g in runs)
     pick = [int(np.argmax(np.diff(w.query_start))), int(np.argmin(w.context_lens)), 5]
     for b in pick:
         q0, q1 = int(w.query_start[b]), int(w.query_start[b + 1])
@@ -639,4 +653,6 @@ def test_prefill_full_size_sampled():
         keep = np.isin(w.fill_blocks, used)
         sub.fill_blocks, sub.fill_valid = w.fill_blocks[keep], w.fill_valid[keep]
         sub.fill_k, sub.fill_v = w.fill_k[keep], w.fill_v[keep]
-        assert float(np.max(np.abs(got[q0:q1] - _prefill_oracle(sub)))) <= TOL, b
+        want = _prefill_oracle(sub)
+        for got in runs:
+            assert float(np.max(np.abs(got[q0:q1] - want))) <= TOL, b
