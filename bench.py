@@ -148,14 +148,20 @@ class Runner:
 
     def step(self, i: int, ev=None, e0: int = 0) -> None:
         """One decode step on layer pool i % layers; with ``ev``, events e0 and
-        e0 + 1 bracket the dominant kernel (the partial or the fused split)."""
+        e0 + 1 bracket the dominant kernel (the partial, the fused split, or the fused step)."""
         abi = self.abi
         k, v, sc = self.pools[i % len(self.pools)]
         stream = self.torch.cuda.current_stream().cuda_stream
-        if self.new is not None:
+        if self.new is not None and self.path != "step":
             abi.kv_cache_write(self.new[0], self.new[1], self.new[2], k, v)
         if ev is not None:
             ev.record(e0, stream)
+        if self.path == "step":
+            abi.paged_decode_step(self.q, self.new[0], self.new[1], k, v, self.tables, self.lens, self.w.scale,
+                                  self.P, self.ws, out=self.out, window=self.spec.window)
+            if ev is not None:
+                ev.record(e0 + 1, stream)
+            return
         if self.path == "balanced":
             abi.paged_decode_attention_balanced(self.q, k, v, self.tables, self.lens, self.w.scale, sc,
                                                 self.bws, out=self.out, window=self.spec.window)
@@ -174,19 +180,28 @@ class Runner:
             abi.paged_decode_attention_reduce(self.tmp_out, self.tmp_lse, self.lens, self.P, self.out,
                                               self.tables.shape[1], window=self.spec.window)
 
+    # Every EVENT_EVERY-th timed step brackets its dominant kernel with a pair
+    # of HIP events: a pair costs ~3-5 us of GPU time, which would otherwise
+    # inflate every step of the wall-clock figure.
+    EVENT_EVERY = 4
+
     def run(self, steps: int, warmup: int):
-        """Returns (seconds per step, [dominant-kernel ms per step])."""
+        """Returns (seconds per step, [dominant-kernel ms of the sampled steps])."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
-        ev = HipEvents(2 * steps)
+        sampled = list(range(0, steps, self.EVENT_EVERY))
+        ev = HipEvents(2 * len(sampled))
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            self.step(warmup + i, ev, 2 * i)
+            if i % self.EVENT_EVERY == 0:
+                self.step(warmup + i, ev, 2 * (i // self.EVENT_EVERY))
+            else:
+                self.step(warmup + i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        kernel_ms = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)]
+        kernel_ms = [ev.elapsed_ms(2 * j, 2 * j + 1) for j in range(len(sampled))]
         ev.close()
         return wall / steps, kernel_ms
 
@@ -459,11 +474,11 @@ def main():
                          ") and print {\"rows\": ...}; no headline line")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other rows of the path (FP8, window, multi-token, quantise, append, copy, write)")
-    ap.add_argument("--path", choices=["pair", "fused", "balanced"], default="pair",
+    ap.add_argument("--path", choices=["pair", "fused", "balanced", "step"], default="pair",
                     help="partial + reduce kernels, the one-launch split with in-kernel merge, or "
                          "equal tile shares per wave + merge")
-    ap.add_argument("--secondary-path", choices=["pair", "fused", "balanced"], default="fused",
-                    help="path for the B=32 line (its fastest: the one-launch split)")
+    ap.add_argument("--secondary-path", choices=["pair", "fused", "balanced", "step"], default="step",
+                    help="path for the B=32 line (its fastest: the fused step, write and attention in one launch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 256 MiB device to device (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -552,7 +567,8 @@ def main():
             "traffic": counters_traffic(args.workload, digest),
             "kernel": {"pair": "paged_decode_persistent, split partial mode",
                        "fused": "paged_decode_persistent, split mode with in-kernel merge",
-                       "balanced": "paged_decode_stream + stream_merge_kernel (both inside the events)"}[args.path],
+                       "balanced": "paged_decode_stream + stream_merge_kernel (both inside the events)",
+                       "step": "paged_decode_persistent, split mode with the new-token write and in-kernel merge"}[args.path],
         },
         "b32": b32,
         "rows": rows,

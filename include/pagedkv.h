@@ -284,6 +284,35 @@ int paged_decode_attention_split(const void* q, const void* k_cache, const void*
 int64_t paged_decode_split_workspace_bytes(const pkv_desc* desc, int32_t partition_size);
 
 /*
+ * paged_decode_step - one decode step in one launch: each sequence's new
+ * token is written into the cache at its position context_lens[b] - 1 (the
+ * new token counts in the context, and is written before attention reads
+ * it), then the attention of paged_decode_attention_split is computed
+ * ("rvllm - A Small LLM Inference Engine in Rust", section "How it's put
+ * together": explicit write positions, then the blocks to read).  The
+ * result equals kv_cache_write of the same rows at those slots followed by
+ * paged_decode_attention_split, bit for bit, in the cache and in out.
+ *
+ *   k_new, v_new     [B][Hkv][D] in the cache dtype (f32, f16 or bf16; an
+ *                    E4M3 cache is rejected, its tokens go through
+ *                    kv_cache_append_e4m3); row b is sequence b's token
+ *   k_cache, v_cache written at slot block_tables[b][(L_b-1)/16]*16 +
+ *                    (L_b-1)%16 for every b with L_b >= 1 (the block the
+ *                    work item holding that position reads; it must not be
+ *                    shared with another sequence)
+ *   other arguments  as paged_decode_attention_split (no kv_scales); the
+ *                    workspace is the split workspace
+ *
+ * The write is done inside the attention kernel by the work item that
+ * reads the block, ahead of its loads, so the step costs one launch
+ * instead of two.
+ */
+int paged_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t partition_size, void* workspace, int64_t workspace_bytes, void* out,
+                      const pkv_desc* desc, void* stream);
+
+/*
  * paged_decode_attention_balanced - the same attention output, with the
  * split-context work cut so that every wave of the GPU gets an equal share
  * of 16-token tiles whatever the mix of context lengths (flash-decoding's

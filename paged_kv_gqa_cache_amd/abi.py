@@ -58,6 +58,7 @@ def _load():
         "paged_decode_attention_reduce": (ctypes.c_int, [P, P, P, I32, P, D, P]),
         "paged_decode_attention_split": (ctypes.c_int, [P, P, P, P, P, F, P, I32, P, I64, P, D, P]),
         "paged_decode_split_workspace_bytes": (ctypes.c_int64, [D, I32]),
+        "paged_decode_step": (ctypes.c_int, [P, P, P, P, P, P, P, F, I32, P, I64, P, D, P]),
         "paged_decode_attention_balanced": (ctypes.c_int, [P, P, P, P, P, F, P, P, I64, P, D, P]),
         "paged_decode_balanced_workspace_bytes": (ctypes.c_int64, [D]),
         "paged_prefill_attention": (ctypes.c_int, [P, P, P, P, P, P, I32, F, P, I32, P, I64, P, D, P]),
@@ -77,7 +78,7 @@ _lib = _load()
 EXPORTED = ("kv_cache_write", "kv_cache_quantize_e4m3", "kv_cache_append_e4m3", "kv_cache_copy_blocks",
             "paged_decode_attention",
             "paged_decode_attention_partial", "paged_decode_attention_reduce",
-            "paged_decode_attention_split", "paged_decode_split_workspace_bytes",
+            "paged_decode_attention_split", "paged_decode_split_workspace_bytes", "paged_decode_step",
             "paged_decode_attention_balanced", "paged_decode_balanced_workspace_bytes",
             "paged_prefill_attention", "paged_prefill_workspace_bytes",
             "paged_decode_num_partitions", "paged_decode_workspace_bytes", "pkv_last_error",
@@ -241,6 +242,20 @@ def paged_decode_attention_split(q, k_cache, v_cache, block_tables, context_lens
     _check("paged_decode_attention_split", _lib.paged_decode_attention_split(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         float(scale), _ptr(kv_scales), int(partition_size), _ptr(workspace), workspace.numel(),
+        _ptr(out), ctypes.byref(desc), _stream(stream)))
+    return out
+
+
+def paged_decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
+                      workspace, out=None, out_dtype=None, stream=None, window=0):
+    """Write each sequence's new token (k_new/v_new [B, Hkv, D]) at position
+    context_lens[b] - 1, then attend (the split path), in one launch."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    desc = _attn_desc(q, k_cache, block_tables, _code(out), window)
+    _check("paged_decode_step", _lib.paged_decode_step(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), float(scale), int(partition_size), _ptr(workspace), workspace.numel(),
         _ptr(out), ctypes.byref(desc), _stream(stream)))
     return out
 

@@ -320,11 +320,11 @@ int paged_decode_attention_partial(const void* q, const void* k_cache, const voi
                     "paged_decode_attention_partial launch");
 }
 
-int paged_decode_attention_split(const void* q, const void* k_cache, const void* v_cache,
-                                 const int32_t* block_tables, const int32_t* context_lens,
-                                 float scale, const float* kv_scales, int32_t partition_size,
-                                 void* workspace, int64_t workspace_bytes, void* out,
-                                 const pkv_desc* desc, void* stream) {
+static int split_common(const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                        const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                        float scale, const float* kv_scales, int32_t partition_size, void* workspace,
+                        int64_t workspace_bytes, void* out, const pkv_desc* desc, void* stream,
+                        const char* what) {
   if (int e = check_desc(desc, true)) return e;
   if (int e = check_attn_types(desc, kv_scales)) return e;
   if (int e = check_partition(partition_size)) return e;
@@ -348,9 +348,33 @@ int paged_decode_attention_split(const void* q, const void* k_cache, const void*
   p.tmp_out = reinterpret_cast<float*>(ws + lay.out_off);
   p.partition_blocks = partition_size / 16;
   p.num_partitions = static_cast<int32_t>(s);
+  p.k_new = k_new;
+  p.v_new = v_new;
   return hip_status(pkv::launch_decode(p, desc->kv_dtype, desc->head_dim, 2,
                                        static_cast<hipStream_t>(stream)),
-                    "paged_decode_attention_split launch");
+                    what);
+}
+
+int paged_decode_attention_split(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 float scale, const float* kv_scales, int32_t partition_size,
+                                 void* workspace, int64_t workspace_bytes, void* out,
+                                 const pkv_desc* desc, void* stream) {
+  return split_common(q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, scale, kv_scales,
+                      partition_size, workspace, workspace_bytes, out, desc, stream,
+                      "paged_decode_attention_split launch");
+}
+
+int paged_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t partition_size, void* workspace, int64_t workspace_bytes, void* out,
+                      const pkv_desc* desc, void* stream) {
+  if (desc && desc->kv_dtype == PKV_E4M3)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_decode_step into an e4m3 cache: use kv_cache_append_e4m3");
+  if (desc && desc->num_seqs > 0 && (!k_new || !v_new))
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  return split_common(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, nullptr,
+                      partition_size, workspace, workspace_bytes, out, desc, stream, "paged_decode_step launch");
 }
 
 int paged_decode_attention_balanced(const void* q, const void* k_cache, const void* v_cache,

@@ -587,6 +587,34 @@ __device__ __forceinline__ void merge_waves(float m_run, float l_run, const f32x
   }
 }
 
+// The fused step's new token of sequence b into slot `off` of physical
+// block `blk`: kv head h's K and V rows of k_new / v_new, laid out as the
+// tiles are (one wave; lane c moves 16-byte chunk c of the rows).
+template <int KVT, int D>
+__device__ __forceinline__ void write_new_token(const DecodeParams& p, int b, int h, int blk, int off) {
+  if constexpr (KVT != KV_E4M3) {   // E4M3 pools take their tokens through kv_cache_append_e4m3
+    constexpr int E = ElemBytes<KVT>::value;
+    typedef typename std::conditional<E == 4, uint32_t, uint16_t>::type Elem;
+    constexpr int X = 16 / E;   // elements per chunk
+    constexpr int CH = D / X;   // chunks per row
+    const int lane = threadIdx.x & 63;
+    if (lane < CH) {
+      const size_t row = (static_cast<size_t>(b) * p.num_kv_heads + h) * D * E + lane * 16;
+      const size_t tile = (static_cast<size_t>(blk) * p.num_kv_heads + h) * kBlockSize * D * E;
+      char* kc = static_cast<char*>(const_cast<void*>(p.k_cache));
+      char* vc = static_cast<char*>(const_cast<void*>(p.v_cache));
+      st16(kc + tile + (static_cast<size_t>(lane) * kBlockSize + off) * 16,
+           ld16(static_cast<const char*>(p.k_new) + row));
+      const u32x4 vv = ld16(static_cast<const char*>(p.v_new) + row);
+      Elem vals[X];
+      __builtin_memcpy(vals, &vv, 16);
+      Elem* vt = reinterpret_cast<Elem*>(vc + tile);
+#pragma unroll
+      for (int i = 0; i < X; ++i) vt[v_tile_elem(off, lane * X + i, 4 / E)] = vals[i];
+    }
+  }
+}
+
 // One work item: sequence b (context length L), kv head h, partition `part`.
 template <int KVT, int D, int NW, int MODE, int PF>
 __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h, int part, int L,
@@ -617,6 +645,18 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
   if (blk0 >= nblk) return;
   const int blk1 = min(nblk, blk0 + p.partition_blocks);
   const bool direct = (MODE == MODE_FINAL) || (MODE == MODE_SPLIT && nparts == 1);
+
+  // Fused decode step: the item that holds position L - 1 writes the new
+  // token there first; the barrier makes the stores visible to every wave
+  // of the workgroup before any of them loads the block.
+  if (p.k_new != nullptr) {
+    const int last = (L - 1) / kBlockSize;
+    if (last >= blk0 && last < blk1) {   // workgroup-uniform
+      const int id = p.block_tables[static_cast<size_t>(b) * p.mbps + last];
+      if (wid == 0 && id >= 0 && id < p.num_blocks) write_new_token<KVT, D>(p, b, h, id, (L - 1) % kBlockSize);
+      __syncthreads();
+    }
+  }
 
   // Blocks of this wave: first + NW * i, i < nmine.
   const int nmine = first < blk1 ? (blk1 - first + NW - 1) / NW : 0;

@@ -25,11 +25,6 @@
 
 namespace pkv {
 
-// Element offset of (token slot t, dim d) inside a V tile, n = 4 / elem bytes.
-__device__ __forceinline__ int v_tile_elem(int t, int d, int n) {
-  return (((((d / (16 * n)) * 4 + t / 4) * 16 + d % 16) * n + (d / 16) % n) * 4 + t % 4);
-}
-
 // One thread per (token, kv head, 16-byte chunk of that head's D elements).
 // K: the chunk is also a contiguous 16 bytes of the K tile (chunk c of token
 // `off` sits at byte (c*16 + off)*16).  V: its elements scatter to their

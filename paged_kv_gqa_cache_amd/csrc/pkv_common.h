@@ -38,6 +38,11 @@ __device__ __forceinline__ To bitcast(const From& x) {
   return __builtin_bit_cast(To, x);
 }
 
+// Element offset of (token slot t, dim d) inside a V tile, n = 4 / elem bytes.
+__device__ __forceinline__ int v_tile_elem(int t, int d, int n) {
+  return (((((d / (16 * n)) * 4 + t / 4) * 16 + d % 16) * n + (d / 16) % n) * 4 + t % 4);
+}
+
 // 16-byte global load / store.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

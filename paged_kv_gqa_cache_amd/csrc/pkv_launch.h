@@ -41,6 +41,11 @@ struct DecodeParams {
   const int32_t* query_start;  // [B + 1]
   int32_t num_query_tokens;
   int32_t tokens_per_pack;     // 16 / G
+  // Fused decode step (null: none): sequence b's new token, K and V rows
+  // [B][Hkv][D] in the cache dtype, written at position L_b - 1 by the work
+  // item that reads that block, before it reads it.
+  const void* k_new;
+  const void* v_new;
 };
 
 struct ReduceParams {

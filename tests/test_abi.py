@@ -191,3 +191,17 @@ def test_prefill_validates_before_touching_the_device():
     rows = 50 * 28 * S
     assert lib.paged_prefill_workspace_bytes(ctypes.byref(d), 50, 512) == (rows * 4 + 255) // 256 * 256 + rows * 128 * 4
     assert lib.paged_prefill_workspace_bytes(ctypes.byref(d), 50, 0) == 0
+
+
+def test_decode_step_rejects_e4m3_and_null_rows():
+    from paged_kv_gqa_cache_amd.abi import PKV_E4M3, PKV_F16, PKV_F32, make_desc, lib
+    import ctypes
+    d = make_desc(2, 8, 2, 128, 16, 4, PKV_F16, PKV_E4M3, PKV_F32)
+    one = ctypes.c_void_p(256)
+    rc = lib().paged_decode_step(one, one, one, one, one, one, one, 1.0, 64, one, 1 << 20, one,
+                                 ctypes.byref(d), None)
+    assert rc != 0 and "e4m3" in abi.last_error()
+    d = make_desc(2, 8, 2, 128, 16, 4, PKV_F16, PKV_F16, PKV_F32)
+    rc = lib().paged_decode_step(one, None, one, one, one, one, one, 1.0, 64, one, 1 << 20, one,
+                                 ctypes.byref(d), None)
+    assert rc != 0 and "null" in abi.last_error()

@@ -656,3 +656,70 @@ def test_prefill_full_size_sampled():
         want = _prefill_oracle(sub)
         for got in runs:
             assert float(np.max(np.abs(got[q0:q1] - want))) <= TOL, b
+
+
+# ------------------------------------------------------ fused decode step ---
+
+def _same_bits(a, b):
+    """Bitwise equality of two caches (unwritten slots hold NaN, which == would reject)."""
+    it = {4: torch.int32, 2: torch.int16, 1: torch.uint8}[a.element_size()]
+    return torch.equal(a.view(it), b.view(it))
+
+
+def _step_pair(w, P, window=0):
+    """(out, k, v) of kv_cache_write + paged_decode_attention_split, and of
+    paged_decode_step, on two copies of the same pool."""
+    from paged_kv_gqa_cache_amd import abi
+    s = w.spec
+    k0, v0, _ = gpu_pool(w, with_new_tokens=False)
+    q, tables, lens = inputs(w)
+    nk, nv = to_dev(w.new_k, s.kv_dtype), to_dev(w.new_v, s.kv_dtype)
+    slots = torch.from_numpy(w.new_slots).cuda()
+    ka, va, kb, vb = k0.clone(), v0.clone(), k0.clone(), v0.clone()
+    ws_a = abi.split_workspace(q, ka, tables, P).zero_()
+    ws_b = abi.split_workspace(q, kb, tables, P).zero_()
+    abi.kv_cache_write(nk, nv, slots, ka, va)
+    out_a = abi.paged_decode_attention_split(q, ka, va, tables, lens, w.scale, None, P, ws_a, window=window)
+    out_b = abi.paged_decode_step(q, nk, nv, kb, vb, tables, lens, w.scale, P, ws_b, window=window)
+    torch.cuda.synchronize()
+    return (out_a, ka, va), (out_b, kb, vb)
+
+
+@pytest.mark.parametrize("name,P", [("tiny", 64), ("qwen25_1p5b", 512), ("qwen25_1p5b", 128), ("tiny", 1024)])
+def test_decode_step_equals_write_then_split(name, P):
+    """One launch writing the new tokens and attending equals the write
+    followed by the split path, bit for bit (cache and output), and the
+    oracle within the tolerance."""
+    _announce("decode step", name, P)
+    w = workloads.generate(name, **REDUCED[name])
+    (oa, ka, va), (ob, kb, vb) = _step_pair(w, P)
+    assert _same_bits(ka, kb) and _same_bits(va, vb)
+    assert torch.equal(oa, ob)
+    assert max_err(ob, oracle_out(w)) <= TOL
+
+
+def test_decode_step_with_window_and_repeated_calls():
+    """Sliding window, and the same workspace reused across calls (the split
+    counters return to zero): every call equals the two-launch result."""
+    _announce("decode step window")
+    from paged_kv_gqa_cache_amd import abi
+    w = workloads.generate("qwen25_1p5b", num_seqs=6, lengths=("uniform", 1, 900))
+    (oa, ka, va), (ob, kb, vb) = _step_pair(w, 128, window=300)
+    assert _same_bits(ka, kb) and _same_bits(va, vb) and torch.equal(oa, ob)
+    q, tables, lens = inputs(w)
+    nk, nv = to_dev(w.new_k, w.spec.kv_dtype), to_dev(w.new_v, w.spec.kv_dtype)
+    ws = abi.split_workspace(q, kb, tables, 128).zero_()
+    for _ in range(5):
+        o = abi.paged_decode_step(q, nk, nv, kb, vb, tables, lens, w.scale, 128, ws, window=300)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ob)
+    assert _same_bits(kb, ka) and _same_bits(vb, va)
+
+
+def test_decode_step_full_size_sampled():
+    """The B=32 Qwen2.5-1.5B-shaped layer at full size through the fused
+    step (the benchmarked configuration): equal to the two-launch result."""
+    _announce("decode step full size")
+    w = workloads.generate("qwen25_1p5b")
+    (oa, ka, va), (ob, kb, vb) = _step_pair(w, 384)
+    assert _same_bits(ka, kb) and _same_bits(va, vb) and torch.equal(oa, ob)
