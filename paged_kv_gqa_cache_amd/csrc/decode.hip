@@ -314,11 +314,15 @@ __device__ __forceinline__ int window_block(int L, int window) { return window_l
 
 // Workgroup-shared state of one work item: the NW waves' softmax states for
 // the cross-wave merge, and the merge ticket of the split mode.
+// The cross-wave merge stages the waves' accumulators through LDS in two
+// passes of half the d-tiles: 16 KiB instead of 32 KiB at D = 128, so three
+// decode workgroups fit on a CU (their registers allow three) instead of two.
+constexpr int kMergePasses = 2;
 template <int NW, int NT>
 struct ItemShared {
   float m[NW][16];
   float l[NW][16];
-  f32x4 o[NW][NT][64];
+  f32x4 o[NW][NT / kMergePasses][64];
   int ticket;
 };
 
@@ -554,29 +558,37 @@ __device__ __forceinline__ void merge_waves(float m_run, float l_run, const f32x
   const int g = lane >> 4;
   const int r = lane & 15;
   if constexpr (NW > 1) {
+    constexpr int NTH = NT / kMergePasses;   // d-tiles staged per pass
     if (g == 0) {
       sm.m[wid][r] = m_run;
       sm.l[wid][r] = l_run;
     }
-#pragma unroll
-    for (int n = 0; n < NT; ++n) sm.o[wid][n][lane] = o[n];
-    __syncthreads();
     float fw[NW];
-    M = sm.m[0][r];
+    float inv = 0.f;
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm.m[w][r]);
-    Lsum = 0.f;
+    for (int pass = 0; pass < kMergePasses; ++pass) {
+      if (pass > 0) __syncthreads();   // the previous pass's reads are done
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      fw[w] = fast_exp2(sm.m[w][r] - M);
-      Lsum += fw[w] * sm.l[w][r];
-    }
-    const float inv = 1.f / Lsum;
-    for (int n = wid; n < NT; n += NW) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < NTH; ++n) sm.o[wid][n][lane] = o[pass * NTH + n];
+      __syncthreads();
+      if (pass == 0) {
+        M = sm.m[0][r];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) acc += fw[w] * sm.o[w][n][lane];
-      emit(n, acc * inv);
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, sm.m[w][r]);
+        Lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          fw[w] = fast_exp2(sm.m[w][r] - M);
+          Lsum += fw[w] * sm.l[w][r];
+        }
+        inv = 1.f / Lsum;
+      }
+      for (int n = wid; n < NTH; n += NW) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc += fw[w] * sm.o[w][n][lane];
+        emit(pass * NTH + n, acc * inv);
+      }
     }
   } else {
     M = m_run;
