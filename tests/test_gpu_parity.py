@@ -352,6 +352,23 @@ def test_balanced_is_deterministic_and_reuses_its_workspace():
     assert max_err(small, oracle_out(sub)) <= TOL
 
 
+@pytest.mark.parametrize("mode", ["single", "split", "fused"])
+def test_more_sequences_than_the_persistent_tables_hold(mode):
+    """2100 sequences (past the 2048 the persistent kernel's LDS tables hold):
+    the one-workgroup-per-item kernel runs, and every row matches."""
+    _announce("many sequences", mode)
+    w = workloads.generate("smollm2_360m", num_seqs=2100, lengths=("uniform", 1, 60))
+    assert max_err(decode(w, gpu_pool(w), mode, partition_size=32), oracle_out(w)) <= TOL
+
+
+def test_decode_step_with_more_sequences_than_the_persistent_tables_hold():
+    _announce("decode step many sequences")
+    w = workloads.generate("qwen25_1p5b", num_seqs=2100, lengths=("uniform", 1, 60))
+    (oa, ka, va), (ob, kb, vb) = _step_pair(w, 32)
+    assert _same_bits(ka, kb) and _same_bits(va, vb) and torch.equal(oa, ob)
+    assert max_err(ob, oracle_out(w)) <= TOL
+
+
 def test_balanced_rejects_too_many_sequences():
     from paged_kv_gqa_cache_amd import abi
     q = torch.zeros(2049, 4, 64, dtype=torch.float16, device="cuda")
