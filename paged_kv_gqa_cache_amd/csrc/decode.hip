@@ -103,6 +103,34 @@ template <int KVT, int D> struct Tile16 {
       o[n] = mma_k16(bitcast<V4>(a), lo, o[n]);
     }
   }
+  // PV over two tiles (a, b) at once on the K = 32 form, at twice the
+  // K = 16 form's rate.  The sum over k takes any order of the 32 tokens as
+  // long as both operands use it: k-slots 8g..8g+3 are tile a's tokens
+  // 4g..4g+3 and 8g+4..8g+7 tile b's, which is what lane (g, r) already
+  // holds of P (p[0..3] for a, p[4..7] for b) and of V (8 bytes per d-tile
+  // and tile), so the operands form without lane exchanges.
+  __device__ static void pv2(f32x4 (&o)[NT], const u32x4 (&va)[NLOAD], const u32x4 (&vb)[NLOAD],
+                             const float (&p)[8]) {
+    V8 hi, lo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const S h = static_cast<S>(p[j]);
+      hi[j] = h;
+      lo[j] = static_cast<S>(p[j] - static_cast<float>(h));
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const u32x4 a = (n & 1) ? u32x4{va[n >> 1].z, va[n >> 1].w, vb[n >> 1].z, vb[n >> 1].w}
+                              : u32x4{va[n >> 1].x, va[n >> 1].y, vb[n >> 1].x, vb[n >> 1].y};
+      o[n] = mma_k32(bitcast<V8>(a), hi, o[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const u32x4 a = (n & 1) ? u32x4{va[n >> 1].z, va[n >> 1].w, vb[n >> 1].z, vb[n >> 1].w}
+                              : u32x4{va[n >> 1].x, va[n >> 1].y, vb[n >> 1].x, vb[n >> 1].y};
+      o[n] = mma_k32(bitcast<V8>(a), lo, o[n]);
+    }
+  }
 };
 template <int D> struct TileOps<KV_F16, D> : Tile16<KV_F16, D> {};
 template <int D> struct TileOps<KV_BF16, D> : Tile16<KV_BF16, D> {};
@@ -390,7 +418,11 @@ struct WaveState {
 // NPK > 1 (the multi-token step): NPK packs of query columns share every
 // tile, each with its own q operand, softmax state and causal limits, so a
 // tile fetched once serves NPK x 16 columns.
-template <int KVT, int D, int PF, bool CAUSAL, int POLICY, int NPK>
+//
+// PAIRS (f16 / bf16 only): tiles go two at a time, PV on the K = 32 form
+// (TileOps::pv2); the ring holds the pair, and the next pair's K loads go
+// out after the QK^T products, its V loads after the PV products.
+template <int KVT, int D, int PF, bool CAUSAL, int POLICY, int NPK, bool PAIRS = false>
 __device__ __forceinline__ void attend_packs(const DecodeParams& p, int b, int h, int L, int lo, int first,
                                              int stride, int count, int ids,
                                              const u32x4 (&qop)[NPK][TileOps<KVT, D>::NQ],
@@ -506,6 +538,98 @@ __device__ __forceinline__ void attend_packs(const DecodeParams& p, int b, int h
   // readlane.  Tiles stream through a ring of PF register buffers: before
   // block j is processed, the loads of block j + PF - 1 are issued, so PF - 1
   // tiles are in flight while the matrix cores work on one.
+  if constexpr (PAIRS) {
+    const auto tile_r = [&](const char* cache, int blk, bool valid) {
+      return make_tile_rsrc(cache + (static_cast<size_t>(blk) * p.num_kv_heads + h) * TILE, valid ? TILE : 0);
+    };
+    auto load_half = [&](u32x4 (&t)[NL], const char* cache, int blk, bool valid) {
+      const auto r = tile_r(cache, blk, valid);
+#pragma unroll
+      for (int m = 0; m < NL; ++m) t[m] = buffer_ld16_policy<POLICY>(r, lane_off[m]);
+    };
+    // Scale and mask one tile's four logits of pack k (tile starting at
+    // position tok0).
+    auto logits = [&](const f32x4& sv, float* x, int tok0, int k) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = sv[j] * p.qk_scale_log2;
+      if (tok0 + kBlockSize > L) {
+        const int nv = L - tok0 - 4 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = (j < nv) ? x[j] : -INFINITY;
+      }
+      if (tok0 < lo) {
+        const int nlo = lo - tok0 - 4 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = (j < nlo) ? -INFINITY : x[j];
+      }
+      if constexpr (CAUSAL) {
+        if (tok0 + kBlockSize - 1 > lim_lo[k]) {
+          const int nc = lim[k] - tok0 - 4 * g;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[j] = (j <= nc) ? x[j] : -INFINITY;
+        }
+      }
+    };
+    u32x4 kb[2][NL], vb[2][NL];
+    for (int base = 0; base < count; base += 64) {
+      const int cnt = min(64, count - base);
+      if (base > 0) ids = (lane < cnt) ? table[first + stride * (base + lane)] : 0;
+      {
+        const int i0 = __builtin_amdgcn_readlane(ids, 0);
+        const int i1 = __builtin_amdgcn_readlane(ids, min(1, cnt - 1));
+        load_half(kb[0], kcache, i0, true);
+        load_half(vb[0], vcache, i0, true);
+        load_half(kb[1], kcache, i1, 1 < cnt);
+        load_half(vb[1], vcache, i1, 1 < cnt);
+      }
+      for (int i = 0; i < cnt; i += 2) {
+        const bool two = i + 1 < cnt;   // else tile b is a zero-size load: V = 0, its logits masked
+        const int tok0 = (first + stride * (base + i)) * kBlockSize;
+        const int tok1 = tok0 + stride * kBlockSize;
+        f32x4 sa[NPK], sb[NPK];
+#pragma unroll
+        for (int k = 0; k < NPK; ++k) {
+          sa[k] = T::qk(kb[0], qop[k]);
+          sb[k] = T::qk(kb[1], qop[k]);
+        }
+        const int n2 = __builtin_amdgcn_readlane(ids, min(i + 2, cnt - 1));
+        const int n3 = __builtin_amdgcn_readlane(ids, min(i + 3, cnt - 1));
+        load_half(kb[0], kcache, n2, i + 2 < cnt);
+        load_half(kb[1], kcache, n3, i + 3 < cnt);
+        if (tok0 + kBlockSize > L) T::mask_v(vb[0], L - tok0 - 4 * g);
+        if (two && tok1 + kBlockSize > L) T::mask_v(vb[1], L - tok1 - 4 * g);
+#pragma unroll
+        for (int k = 0; k < NPK; ++k) {
+          float x[8];
+          logits(sa[k], x, tok0, k);
+          logits(sb[k], x + 4, tok1, k);
+          if (!two) {
+#pragma unroll
+            for (int j = 4; j < 8; ++j) x[j] = -INFINITY;
+          }
+          WaveState<NT>& sk = st[k];
+          const float bm = max_over_groups(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                                 fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
+          if (__any(bm > sk.m + kSlack)) {   // lazy rescaling, as in the one-tile step
+            const float m_new = fmaxf(sk.m, bm);
+            const float alpha = fast_exp2(sk.m - m_new);
+            sk.m = m_new;
+            sk.l *= alpha;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) sk.o[n] *= alpha;
+          }
+          float pr[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pr[j] = fast_exp2(x[j] - sk.m);
+          sk.l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+          T::pv2(sk.o, vb[0], vb[1], pr);
+        }
+        load_half(vb[0], vcache, n2, i + 2 < cnt);
+        load_half(vb[1], vcache, n3, i + 3 < cnt);
+      }
+    }
+    return;
+  }
   u32x4 kb[PF][NL], vb[PF][NL];
   float ks[PF], vs[PF];
   for (int base = 0; base < count; base += 64) {
@@ -942,7 +1066,7 @@ __device__ __forceinline__ void prefill_prefetch(const DecodeParams& p, int b, i
 // One work item: sequence b, kv head h, packs grp*NPK .. grp*NPK + NPK - 1
 // (TP = tokens_per_pack tokens each), partition `part` of the blocks up to
 // the group's last token.
-template <int KVT, int D, int NW, int MODE, int PF, int NPK>
+template <int KVT, int D, int NW, int MODE, int PF, int NPK, bool PAIRS>
 __device__ __forceinline__ void prefill_item(const DecodeParams& p, int b, int h, int grp, int part, int L,
                                              QueryRows qrow, const PackPrefetch<KVT, D, NPK>& pf,
                                              ItemShared<NW, D / 16>& sm) {
@@ -975,7 +1099,7 @@ __device__ __forceinline__ void prefill_item(const DecodeParams& p, int b, int h
   WaveState<NT> st[NPK];
 #pragma unroll
   for (int k = 0; k < NPK; ++k) st[k].reset(-1e30f);   // finite: a column may see no position in a wave's blocks
-  attend_packs<KVT, D, PF, true, 0, NPK>(p, b, h, l_item, 0, first, NW, nmine, pf.ids, pf.qop, st, pos);
+  attend_packs<KVT, D, PF, true, 0, NPK, PAIRS>(p, b, h, l_item, 0, first, NW, nmine, pf.ids, pf.qop, st, pos);
 
 #pragma unroll
   for (int k = 0; k < NPK; ++k) {
@@ -998,8 +1122,8 @@ __device__ __forceinline__ void prefill_item(const DecodeParams& p, int b, int h
 
 // Persistent form of the multi-token step, laid out like
 // paged_decode_persistent: LDS prefix sums of each sequence's items, XCD
-// ranges, the next item's ids and q prefetched during the current one.
-template <int KVT, int D, int NW, int MODE, int PF, int NPK>
+// ranges.
+template <int KVT, int D, int NW, int MODE, int PF, int NPK, bool PAIRS>
 __global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const DecodeParams p) {
   __shared__ ItemShared<NW, D / 16> sm;
   __shared__ int s_cum[kMaxSeqsPersistent + 1];   // items before sequence b
@@ -1071,23 +1195,20 @@ __global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const Decode
   };
   int n = lo + static_cast<int>(blockIdx.x) / kXcds;
   if (n >= hi) return;
-  int b, h, pack, part, b2, h2, pack2, part2;
-  PackPrefetch<KVT, D, NPK> cur, nxt;
-  locate(n, b, h, pack, part);
-  prefill_prefetch<KVT, D, NW, NPK>(p, b, h, pack, part, QueryRows{s_q0[b], s_nq[b]}, cur);
+  // An item's ids and q load at its start: items here are long (many
+  // tiles per wave), so the one exposed latency costs little, and holding
+  // the next item's q operands through the current one would take 32
+  // registers (measured: no faster with them).
   while (true) {
-    const int n2 = n + per_xcd;
-    locate(min(n2, hi - 1), b2, h2, pack2, part2);
-    prefill_prefetch<KVT, D, NW, NPK>(p, b2, h2, pack2, part2, QueryRows{s_q0[b2], s_nq[b2]}, nxt);
-    prefill_item<KVT, D, NW, MODE, PF, NPK>(p, b, h, pack, part, s_len[b], QueryRows{s_q0[b], s_nq[b]}, cur, sm);
+    int b, h, pack, part;
+    locate(n, b, h, pack, part);
+    PackPrefetch<KVT, D, NPK> cur;
+    prefill_prefetch<KVT, D, NW, NPK>(p, b, h, pack, part, QueryRows{s_q0[b], s_nq[b]}, cur);
+    prefill_item<KVT, D, NW, MODE, PF, NPK, PAIRS>(p, b, h, pack, part, s_len[b], QueryRows{s_q0[b], s_nq[b]}, cur,
+                                                   sm);
     __syncthreads();   // the next item reuses the merge state
-    if (n2 >= hi) break;
-    n = n2;
-    b = b2;
-    h = h2;
-    pack = pack2;
-    part = part2;
-    cur = nxt;
+    n += per_xcd;
+    if (n >= hi) break;
   }
 }
 
@@ -1460,13 +1581,29 @@ hipError_t launch_stream_merge(const ReduceParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <auto KERNEL>
+static hipError_t launch_prefill_kernel(const DecodeParams& p, hipStream_t stream) {
+  const int grid = std::max(kXcds, resident_workgroups<KERNEL>(kWaves * 64) / kXcds * kXcds);
+  hipLaunchKernelGGL(KERNEL, dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int KVT, int D, int MODE>
 static hipError_t launch_prefill_t(const DecodeParams& p, hipStream_t stream) {
   constexpr int kPf = ring_depth<KVT, D>();
-  constexpr auto kernel = paged_prefill_persistent<KVT, D, kWaves, MODE, kPf, kPacksPerWave>;
-  const int grid = std::max(kXcds, resident_workgroups<kernel>(kWaves * 64) / kXcds * kXcds);
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kWaves * 64), 0, stream, p);
-  return hipGetLastError();
+  // Tiles in pairs (PV on the K = 32 form) for 16-bit caches when the
+  // sequences average 16 or more query rows, where the step is bound by
+  // the matrix cores and the softmax (chunked prefill, 137 rows per
+  // sequence: 223 -> 202 us).  With a few rows per sequence it is bound by
+  // memory, and the one-tile path keeps more loads in flight (speculative
+  // verification, 4 rows: 71 us, 74 with pairs); with one row per sequence
+  // it also rounds exactly as the decode kernels do.
+  if constexpr (KVT == KV_F16 || KVT == KV_BF16) {
+    if (static_cast<int64_t>(p.num_query_tokens) >= 16LL * p.num_seqs)
+      return launch_prefill_kernel<paged_prefill_persistent<KVT, D, kWaves, MODE, kPf, kPacksPerWave, true>>(p,
+                                                                                                           stream);
+  }
+  return launch_prefill_kernel<paged_prefill_persistent<KVT, D, kWaves, MODE, kPf, kPacksPerWave, false>>(p, stream);
 }
 
 template <int KVT>

@@ -608,6 +608,22 @@ def test_prefill_matches_oracle(kw, P):
     assert max_err(_prefill_gpu(w, gpu_pool(w), P), _prefill_oracle(w)) <= TOL
 
 
+@pytest.mark.parametrize("rows", [(16, 48), (1, 6)])
+@pytest.mark.parametrize("kw", [dict(), dict(num_q_heads=8, num_kv_heads=4, q_dtype="f16", kv_dtype="f16"),
+                                dict(num_q_heads=32, num_kv_heads=2), dict(num_q_heads=4, num_kv_heads=4)])
+def test_prefill_both_tile_paths(kw, rows):
+    """16-bit caches take tiles in pairs (PV on the K = 32 form) when the
+    sequences average 16 or more query rows, one at a time otherwise: each
+    path against the oracle, with odd and even tile counts per wave."""
+    _announce("prefill tile paths", kw, rows)
+    w = workloads.generate("qwen25_7b_chunk", num_seqs=7, lengths=("uniform", 48, 600),
+                           query_tokens=("uniform", *rows), **kw)
+    avg = w.query_start[-1] / len(w.context_lens)
+    assert (avg >= 16) == (rows[0] >= 16)
+    for P in (0, 64):
+        assert max_err(_prefill_gpu(w, gpu_pool(w), P), _prefill_oracle(w)) <= TOL, P
+
+
 @pytest.mark.parametrize("P", [0, 64])
 @pytest.mark.parametrize("kw", [dict(), dict(num_q_heads=32, num_kv_heads=2)])
 def test_prefill_partial_pack_groups(kw, P):
