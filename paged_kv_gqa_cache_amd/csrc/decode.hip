@@ -784,8 +784,10 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
 
   // Fused decode step: the item that holds position L - 1 writes the new
   // token there first; the barrier makes the stores visible to every wave
-  // of the workgroup before any of them loads the block.
-  if (p.k_new != nullptr) {
+  // of the workgroup before any of them loads the block.  Only the split
+  // mode carries new tokens (paged_decode_step); compiled out of the
+  // others, the single-pass kernel fits three workgroups per CU.
+  if (MODE == MODE_SPLIT && p.k_new != nullptr) {
     const int last = (L - 1) / kBlockSize;
     if (last >= blk0 && last < blk1) {   // workgroup-uniform
       const int id = p.block_tables[static_cast<size_t>(b) * p.mbps + last];
