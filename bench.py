@@ -458,6 +458,43 @@ def measure_rows(args, only=None) -> dict:
     return rows
 
 
+def read_ceiling(gib: int = 4, calls: int = 10) -> dict:
+    """Read bandwidth this GPU sustains: pkv_read_bandwidth_probe (16-byte
+    non-temporal loads, four in flight per thread) over a fresh buffer,
+    timed with HIP events; the practical ceiling beside the published peak."""
+    import torch
+    from paged_kv_gqa_cache_amd import abi
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    out = torch.empty(4096, dtype=torch.int32, device="cuda")
+
+    def call():
+        abi.pkv_read_bandwidth_probe(buf, out)
+
+    ms = time_calls(call, calls, warmup=2)
+    del buf, out
+    torch.cuda.empty_cache()
+    return {"GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes, "calls": calls,
+            "what": "pkv_read_bandwidth_probe: one read of a 4 GiB buffer, 16-byte non-temporal loads, "
+                    "4 in flight per thread, 2 workgroups of 256 per CU; HIP events around 10 back-to-back calls"}
+
+
+def latency_stats(ms_samples) -> dict:
+    """Median, p20, p80 and minimum of the sampled kernel durations (us)."""
+    import numpy as np
+    a = np.asarray(ms_samples, dtype=np.float64) * 1e3
+    return {"median": round(float(np.median(a)), 2), "p20": round(float(np.percentile(a, 20)), 2),
+            "p80": round(float(np.percentile(a, 80)), 2), "min": round(float(a.min()), 2), "samples": int(a.size)}
+
+
+def environment() -> dict:
+    """What the run measured on: GPU, architecture, compute units, versions."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""), "compute_units": props.multi_processor_count,
+            "torch": torch.__version__, "hip": torch.version.hip}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -467,6 +504,8 @@ def main():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--layers", type=int, default=4, help="layer pools rotated through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the streaming-read probe (the measured read ceiling, context for the roofline)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-torch-reference", action="store_true",
                     help="skip timing the materialising PyTorch reference of the headline step")
@@ -577,6 +616,12 @@ def main():
         "kernel_source_digest": digest,
         "library": abi.version(),
     }
+    line["dominant_kernel_us_stats"] = latency_stats(part_ms)
+    line["environment"] = environment()
+    if not args.no_read_ceiling:
+        ceiling = read_ceiling()
+        ceiling["kernel_frac_of_it"] = round(achieved / ceiling["GBps"], 4)
+        line["read_ceiling"] = ceiling
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(line), flush=True)

@@ -394,6 +394,22 @@ const char* pkv_last_error(void);
 /* Library version string.  */
 const char* pkv_version(void);
 
+/*
+ * pkv_read_bandwidth_probe - a measurement aid, not part of the attention
+ * path: reads `bytes` of device memory at src once with 16-byte
+ * non-temporal loads (four in flight per thread, two 256-thread workgroups
+ * per compute unit) and writes one XOR-folded word per workgroup to out.
+ * Timing it (events on `stream`) gives the read bandwidth this GPU
+ * sustains: a practical ceiling, beside the published HBM peak, for the
+ * decode kernels' byte rates.  The pages define no such operation; it
+ * belongs to the measurement, not to the method.
+ *   src        device, 16-byte aligned, bytes > 0 and a multiple of 16
+ *   out        device, out_words words (caller-owned); the grid is
+ *              min(out_words, 2 x CUs) workgroups
+ * Errors: PKV_ERR_INVALID_ARG on a null pointer, misalignment or a bad size.
+ */
+int pkv_read_bandwidth_probe(const void* src, int64_t bytes, uint32_t* out, int32_t out_words, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,7 @@ def _load():
         "paged_decode_workspace_bytes": (ctypes.c_int64, [D, I32]),
         "pkv_last_error": (ctypes.c_char_p, []),
         "pkv_version": (ctypes.c_char_p, []),
+        "pkv_read_bandwidth_probe": (ctypes.c_int, [P, I64, P, I32, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -82,7 +83,7 @@ EXPORTED = ("kv_cache_write", "kv_cache_quantize_e4m3", "kv_cache_append_e4m3", 
             "paged_decode_attention_balanced", "paged_decode_balanced_workspace_bytes",
             "paged_prefill_attention", "paged_prefill_workspace_bytes",
             "paged_decode_num_partitions", "paged_decode_workspace_bytes", "pkv_last_error",
-            "pkv_version")
+            "pkv_version", "pkv_read_bandwidth_probe")
 
 
 def lib():
@@ -95,6 +96,15 @@ def version() -> str:
 
 def last_error() -> str:
     return _lib.pkv_last_error().decode()
+
+
+def pkv_read_bandwidth_probe(buf: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """Read every byte of device tensor ``buf`` once (measurement aid: the
+    GPU's sustained read rate); ``out`` (int32, device) receives one
+    XOR-folded word per workgroup."""
+    _check("pkv_read_bandwidth_probe", _lib.pkv_read_bandwidth_probe(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(out), out.numel(), _stream(stream)))
+    return out
 
 
 def _check(func: str, status: int) -> None:

@@ -156,6 +156,15 @@ const char* pkv_last_error(void) { return g_err; }
 
 const char* pkv_version(void) { return "pagedkv 0.1.0 gfx950"; }
 
+int pkv_read_bandwidth_probe(const void* src, int64_t bytes, uint32_t* out, int32_t out_words, void* stream) {
+  if (!src || !out) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (bytes <= 0 || bytes % 16 != 0) return fail(PKV_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0) return fail(PKV_ERR_INVALID_ARG, "src must be 16-byte aligned");
+  if (out_words <= 0) return fail(PKV_ERR_INVALID_ARG, "out_words must be positive");
+  return hip_status(pkv::launch_read_probe(src, bytes, out, out_words, static_cast<hipStream_t>(stream)),
+                    "pkv_read_bandwidth_probe launch");
+}
+
 int64_t paged_decode_num_partitions(const pkv_desc* desc, int32_t partition_size) {
   if (check_desc(desc, false) || check_partition(partition_size)) return -1;
   return partitions(desc, partition_size);

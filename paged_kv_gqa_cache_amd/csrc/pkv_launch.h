@@ -122,5 +122,6 @@ hipError_t launch_kv_write(const WriteParams& p, hipStream_t stream);
 hipError_t launch_quantize_e4m3(const QuantParams& p, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
 hipError_t launch_append_e4m3(const AppendParams& p, hipStream_t stream);
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, int32_t out_words, hipStream_t stream);
 
 }  // namespace pkv

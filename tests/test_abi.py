@@ -205,3 +205,16 @@ def test_decode_step_rejects_e4m3_and_null_rows():
     rc = lib().paged_decode_step(one, None, one, one, one, one, one, 1.0, 64, one, 1 << 20, one,
                                  ctypes.byref(d), None)
     assert rc != 0 and "null" in abi.last_error()
+
+
+def test_read_probe_validates_before_launching():
+    """The read-bandwidth probe rejects a null pointer, a size that is not a
+    positive multiple of 16 and a misaligned source, without launching."""
+    from paged_kv_gqa_cache_amd.abi import lib
+    buf, out = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    probe = lib().pkv_read_bandwidth_probe
+    assert probe(None, 1024, out, 16, None) == INVALID and "null" in abi.last_error()
+    assert probe(buf, 1000, out, 16, None) == INVALID and "multiple of 16" in abi.last_error()
+    assert probe(buf, 0, out, 16, None) == INVALID
+    assert probe(ctypes.c_void_p(4100), 1024, out, 16, None) == INVALID and "aligned" in abi.last_error()
+    assert probe(buf, 1024, out, 0, None) == INVALID

@@ -756,3 +756,22 @@ def test_decode_step_full_size_sampled():
     w = workloads.generate("qwen25_1p5b")
     (oa, ka, va), (ob, kb, vb) = _step_pair(w, 384)
     assert _same_bits(ka, kb) and _same_bits(va, vb) and torch.equal(oa, ob)
+
+
+# -------------------------------------------------- read-bandwidth probe ---
+
+@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 48, 3 << 20])
+def test_read_probe_reads_every_word(nbytes):
+    """The measurement probe's per-workgroup XOR words fold to the XOR of
+    every 32-bit word of the buffer (each word read exactly once), for a
+    single 16-byte chunk, a ragged size and a multi-megabyte buffer."""
+    _announce("read probe", nbytes)
+    from paged_kv_gqa_cache_amd import abi
+    rng = np.random.default_rng(nbytes)
+    words = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    out = torch.zeros(2048, dtype=torch.int32, device="cuda")
+    abi.pkv_read_bandwidth_probe(buf, out)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words)
