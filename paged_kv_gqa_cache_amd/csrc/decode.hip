@@ -33,7 +33,9 @@
 //    B-operand layout P^T needs for the PV product: the softmax needs only a
 //    lane-local max over 4 values plus two cross-group shuffles per block.
 //  * P stays fp32-accurate: 16-bit PV uses P = hi + lo (two 16-bit parts,
-//    two MFMAs), so only V's own rounding is in the product.
+//    two MFMAs), so only V's own rounding is in the product.  The
+//    multi-token step, when it has many rows per sequence, takes tiles in
+//    pairs and runs PV on the K = 32 form (twice the rate of K = 16).
 //  * E4M3 codes decode to fp16 exactly with the packed hardware conversion;
 //    the block's K scale folds into its logit factor, its V scale into P.
 //  * Softmax runs in base 2 (log2 e folded into the scale).
@@ -1031,7 +1033,8 @@ struct QueryRows {
 };
 
 // A work item's loads that do not depend on its math, for NPK packs: the
-// wave's first 64 block ids and each pack's q operand.
+// wave's first 64 block ids and each pack's q operand, issued at the
+// item's start.
 template <int KVT, int D, int NPK>
 struct PackPrefetch {
   int ids;
