@@ -162,6 +162,12 @@ class Runner:
             if ev is not None:
                 ev.record(e0 + 1, stream)
             return
+        if self.path == "single":
+            abi.paged_decode_attention(self.q, k, v, self.tables, self.lens, self.w.scale, sc, out=self.out,
+                                       window=self.spec.window)
+            if ev is not None:
+                ev.record(e0 + 1, stream)
+            return
         if self.path == "balanced":
             abi.paged_decode_attention_balanced(self.q, k, v, self.tables, self.lens, self.w.scale, sc,
                                                 self.bws, out=self.out, window=self.spec.window)
@@ -313,8 +319,8 @@ def torch_materialising(r, steps: int) -> dict:
                     "matmul (context for the materialising-reference comparison; not part of the path)"}
 
 
-ROW_NAMES = ("fp8_e4m3_decode", "e4m3_bulk_quantise", "e4m3_append", "sliding_window", "chunked_prefill",
-             "spec_verify_4", "copy_blocks", "kv_slot_write")
+ROW_NAMES = ("single_pass", "fp8_e4m3_decode", "e4m3_bulk_quantise", "e4m3_append", "sliding_window",
+             "chunked_prefill", "spec_verify_4", "copy_blocks", "kv_slot_write")
 
 
 def measure_rows(args, only=None) -> dict:
@@ -331,18 +337,40 @@ def measure_rows(args, only=None) -> dict:
     steps, warm = max(10, args.steps // 2), max(3, args.warmup // 2)
     want = (lambda k: True) if not only else (lambda k: k in only)
 
+    # The headline layer through the single-pass entry point (no workspace,
+    # one work item per sequence and kv head: the longest context bounds it).
+    if want("single_pass"):
+        r = Runner(HEADLINE, args.layers, None, "pair")
+        it = [0]
+
+        def single():
+            k, v, sc = r.pools[it[0] % len(r.pools)]
+            it[0] += 1
+            abi.paged_decode_attention(r.q, k, v, r.tables, r.lens, r.w.scale, sc, out=r.out, window=r.spec.window)
+
+        ms = time_calls(single, steps)
+        rows["single_pass"] = hbm_row(r.unique_bytes, ms, "unique K/V bytes read per step")
+        rows["single_pass"]["workload"] = f"{HEADLINE}: {DESCRIPTIONS[HEADLINE]}; paged_decode_attention (one pass)"
+        del r
+        torch.cuda.empty_cache()
+
     # FP8 E4M3 decode (per-(block, kv head) scales) and the sliding window:
     # balanced schedule, kernel time = stream kernel + merge (both in the events).
-    for key, name, P in (("fp8_e4m3_decode", "qwen25_7b_fp8", 512), ("sliding_window", "gemma_sliding", 512)):
+    # Each on its fastest path (measured: FP8 balanced 94 us, single pass 96,
+    # pair P = 2048 97; sliding window single pass 88 us, balanced 94, pair
+    # 106-112).  The window's items are equal (1024 positions each), so one
+    # pass per (sequence, kv head) is balanced without a merge kernel.
+    for key, name, P, path in (("fp8_e4m3_decode", "qwen25_7b_fp8", 512, "balanced"),
+                               ("sliding_window", "gemma_sliding", None, "single")):
         extra = ("e4m3_bulk_quantise", "e4m3_append") if name == "qwen25_7b_fp8" else ()
         if not any(want(k) for k in (key,) + extra):
             continue
-        r = Runner(name, args.layers, P, "balanced")
+        r = Runner(name, args.layers, P, path)
         if want(key):
             t, part = r.run(steps, warm)
             ms = sum(part) / len(part)
             row = hbm_row(r.unique_bytes, ms, "unique K/V (+ E4M3 scales) bytes read per step")
-            row.update({"workload": f"{name}: {DESCRIPTIONS[name]}", "path": "balanced",
+            row.update({"workload": f"{name}: {DESCRIPTIONS[name]}", "path": path,
                         "us_per_step": round(t * 1e6, 2), "step_GBps": round(r.unique_bytes / t / 1e9, 1)})
             rows[key] = row
         if name == "qwen25_7b_fp8":
@@ -514,7 +542,7 @@ def main():
                          ") and print {\"rows\": ...}; no headline line")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other rows of the path (FP8, window, multi-token, quantise, append, copy, write)")
-    ap.add_argument("--path", choices=["pair", "fused", "balanced", "step"], default="pair",
+    ap.add_argument("--path", choices=["pair", "fused", "balanced", "step", "single"], default="pair",
                     help="partial + reduce kernels, the one-launch split with in-kernel merge, or "
                          "equal tile shares per wave + merge")
     ap.add_argument("--secondary-path", choices=["pair", "fused", "balanced", "step"], default="step",
@@ -608,7 +636,8 @@ def main():
             "kernel": {"pair": "paged_decode_persistent, split partial mode",
                        "fused": "paged_decode_persistent, split mode with in-kernel merge",
                        "balanced": "paged_decode_stream + stream_merge_kernel (both inside the events)",
-                       "step": "paged_decode_persistent, split mode with the new-token write and in-kernel merge"}[args.path],
+                       "step": "paged_decode_persistent, split mode with the new-token write and in-kernel merge",
+                       "single": "paged_decode_persistent, single-pass mode"}[args.path],
         },
         "b32": b32,
         "rows": rows,
