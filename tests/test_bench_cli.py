@@ -1,0 +1,30 @@
+"""bench.py's host side (no GPU): the one-GPU contract, the latency
+statistics, and that the committed HBM-counter summary belongs to the
+committed kernel sources (else the bench line's roofline.traffic is null)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_latency_stats():
+    st = bench.latency_stats([0.010, 0.020, 0.030, 0.040, 0.050])   # ms
+    assert st == {"median": 30.0, "p20": 18.0, "p80": 42.0, "min": 10.0, "samples": 5}
+
+
+def test_committed_counters_match_the_kernel_sources():
+    traffic = bench.counters_traffic(bench.HEADLINE, bench.source_digest())
+    assert traffic is not None, "profiles/ counter summary was taken from other kernel sources"
+    assert 250e6 < traffic < 400e6
