@@ -71,6 +71,18 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const WriteParams p) {
 // scale = fp32(amax / 448) over the block's valid slots (1 if amax is 0);
 // code = nearest-even E4M3 of clamp(fp32(x / scale), -448, 448); slots at or
 // past valid_tokens get code 0.
+//
+// The quotient is formed as fp32((double)x * (1 / (double)scale)), which
+// equals the correctly rounded fp32 x / scale wherever that is a normal
+// number: the double product is within 2^-52 (relative) of x / scale, while
+// a quotient of two 24-bit numbers lies either on an fp32 value or at least
+// ~2^-49 (relative) away from the nearest rounding midpoint (it is never on
+// one: x = scale * midpoint would need the midpoint's 25-bit odd
+// significand).  Below 2^-126 the two may differ, but every such value
+// encodes as a zero code of the same sign either way.  gfx950's
+// v_cvt_pk_fp8_f32 then rounds two clamped quotients to OCP E4M3 codes,
+// ties to even.  Source reads and code writes stream (non-temporal): each
+// byte is touched once.
 template <int D>
 __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const QuantParams p) {
   constexpr int TB = kBlockSize * D;         // bytes of codes in one tile
@@ -78,61 +90,67 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const QuantParams p)
   constexpr int C4 = D / 4;                  // 16-byte pieces per source row
   __shared__ __align__(16) unsigned char img[4][TB];
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int Hkv = p.num_kv_heads;
-  const int64_t ntiles = static_cast<int64_t>(p.num_src_blocks) * Hkv * 2;
-  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + wid;
-  const bool live = tile < ntiles;   // wave-uniform
-  const int h = live ? static_cast<int>(tile % Hkv) : 0;
-  const bool is_v = live && ((tile / Hkv) % 2) != 0;
-  const int i = live ? static_cast<int>(tile / (2 * Hkv)) : 0;
-  float scale = 1.0f;
-  if (live) {
-    const int valid = max(0, min(p.valid_tokens[i], kBlockSize));
-    const float* src = (is_v ? p.v_src : p.k_src) + (static_cast<size_t>(i) * kBlockSize * Hkv + h) * D;
-    u32x4 x[NJ];
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // tile indices stay scalar
+  const uint32_t Hkv = static_cast<uint32_t>(p.num_kv_heads);
+  const uint64_t ntiles = static_cast<uint64_t>(p.num_src_blocks) * Hkv * 2;
+  const uint64_t tile = static_cast<uint64_t>(blockIdx.x) * 4 + wid;
+  if (tile >= ntiles) return;   // wave-uniform; no workgroup barrier follows
+  uint32_t pair;                // block * 2 + (V ? 1 : 0)
+  if (ntiles <= 0xFFFFFFFFull) pair = static_cast<uint32_t>(tile) / Hkv;
+  else pair = static_cast<uint32_t>(tile / Hkv);
+  pair = __builtin_amdgcn_readfirstlane(pair);   // the division runs on the VALU
+  const int h = static_cast<int>(tile - static_cast<uint64_t>(pair) * Hkv);
+  const bool is_v = (pair & 1u) != 0;
+  const int i = static_cast<int>(pair >> 1);
+  const int valid = __builtin_amdgcn_readfirstlane(max(0, min(p.valid_tokens[i], kBlockSize)));
+  // Head h's rows of the block: row t at t * Hkv * D floats.  The descriptor
+  // ends after row valid - 1, so the rows past it read as zeros.
+  const float* src = (is_v ? p.v_src : p.k_src) + (static_cast<size_t>(i) * kBlockSize * Hkv + h) * D;
+  const auto rsrc = make_tile_rsrc(src, valid > 0 ? ((valid - 1) * static_cast<int>(Hkv) + 1) * D * 4 : 0);
+  u32x4 x[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = j * 64 + lane;
-      const int t = e / C4;
-      x[j] = t < valid ? ld16(src + static_cast<size_t>(t) * Hkv * D + 4 * (e % C4)) : u32x4{0u, 0u, 0u, 0u};
-    }
-    float amax = 0.f;
+  for (int j = 0; j < NJ; ++j) {
+    const int e = j * 64 + lane;
+    x[j] = buffer_ld16_policy<kStreamLoad>(rsrc, static_cast<uint32_t>((e / C4) * static_cast<int>(Hkv) * D * 4 + (e % C4) * 16));
+  }
+  float amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fabsf(__uint_as_float(x[j][k])));
+    for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fabsf(__uint_as_float(x[j][k])));
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    scale = amax > 0.f ? amax / 448.0f : 1.0f;
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+  const double inv = 1.0 / static_cast<double>(scale);
+  unsigned char* im = img[wid];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = j * 64 + lane;
-      const int t = e / C4;
-      const int d = 4 * (e % C4);
-      uint32_t code[4];
+  for (int j = 0; j < NJ; ++j) {
+    const int e = j * 64 + lane;
+    const int t = e / C4;
+    const int d = 4 * (e % C4);
+    float y[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float y = fminf(fmaxf(__uint_as_float(x[j][k]) / scale, -448.0f), 448.0f);
-        code[k] = t < valid ? f32_to_e4m3(y) : 0u;
-      }
-      if (!is_v) {   // K: dims d..d+3 of token t are 4 consecutive bytes of one 16-byte chunk
-        *reinterpret_cast<uint32_t*>(&img[wid][((d / 16) * kBlockSize + t) * 16 + d % 16]) =
-            code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-      } else {       // V: each dim lands in its own chunk (tokens are the fast index there)
+    for (int k = 0; k < 4; ++k)
+      y[k] = fminf(fmaxf(static_cast<float>(static_cast<double>(__uint_as_float(x[j][k])) * inv), -448.0f), 448.0f);
+    // Slots past valid_tokens loaded as +0 and so encode as code 0.
+    uint32_t w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false));
+    w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], static_cast<int>(w), true));
+    if (!is_v) {   // K: dims d..d+3 of token t are 4 consecutive bytes of one 16-byte chunk
+      *reinterpret_cast<uint32_t*>(&im[((d / 16) * kBlockSize + t) * 16 + d % 16]) = w;
+    } else {       // V: each dim lands in its own chunk (tokens are the fast index there)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) img[wid][v_tile_elem(t, d + k, 4)] = static_cast<unsigned char>(code[k]);
-      }
+      for (int k = 0; k < 4; ++k) im[v_tile_elem(t, d + k, 4)] = static_cast<unsigned char>(w >> (8 * k));
     }
   }
-  __syncthreads();
-  if (live) {
-    const int blk = p.block_ids[i];
-    char* dst = static_cast<char*>(is_v ? p.v_cache : p.k_cache) + (static_cast<size_t>(blk) * Hkv + h) * TB;
+  // The wave reads back only the image it wrote: LDS operations of one wave
+  // complete in order, so a wave-level scheduling barrier is enough.
+  __builtin_amdgcn_wave_barrier();
+  const int blk = p.block_ids[i];
+  char* dst = static_cast<char*>(is_v ? p.v_cache : p.k_cache) + (static_cast<size_t>(blk) * Hkv + h) * TB;
 #pragma unroll
-    for (int off = lane * 16; off < TB; off += 1024) st16(dst + off, *reinterpret_cast<const u32x4*>(&img[wid][off]));
-    if (lane == 0) p.kv_scales[((is_v ? static_cast<size_t>(p.num_blocks) : 0) + blk) * Hkv + h] = scale;
-  }
+  for (int off = lane * 16; off < TB; off += 1024)
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&im[off]), reinterpret_cast<u32x4*>(dst + off));
+  if (lane == 0) p.kv_scales[((is_v ? static_cast<size_t>(p.num_blocks) : 0) + blk) * Hkv + h] = scale;
 }
 
 // One workgroup (D threads) per (token, kv head, K-or-V); thread d owns dim

@@ -109,6 +109,43 @@ def test_quantize_e4m3_is_bit_exact(kw):
     assert np.array_equal(s_g.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
 
 
+def test_quantize_e4m3_rounding_boundaries():
+    """Every E4M3 value, every midpoint between neighbouring values and the
+    fp32 numbers on either side of it, both signs, signed zeros and
+    subnormal quotients.  Each (block, kv head) tile holds a 448, so its
+    scale is exactly 1 and the quotients are the crafted values themselves:
+    the codes then test the encoder's rounding (ties to even) alone."""
+    from oracle import e4m3
+    from paged_kv_gqa_cache_amd import abi
+    _announce("quantize rounding boundaries")
+    pos = np.array([e4m3.decode_value(c) for c in range(0x7F)], dtype=np.float64)   # 0 .. 448
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)                          # exact in fp32
+    vals = np.concatenate([pos.astype(np.float32), mids, np.nextafter(mids, np.float32(np.inf)),
+                           np.nextafter(mids, np.float32(0)),
+                           np.float32([2.0 ** -149, 2.0 ** -126, 2.0 ** -10, 3 * 2.0 ** -11, 0.0])])
+    vals = np.concatenate([vals, -vals])
+    n, hkv, d, nb = 6, 2, 128, 9
+    xk = np.resize(vals, n * 16 * hkv * d).astype(np.float32).reshape(n, 16, hkv, d)
+    xv = np.resize(vals[::-1], n * 16 * hkv * d).astype(np.float32).reshape(n, 16, hkv, d)
+    xk[:, 0, :, 0] = 448.0
+    xv[:, 0, :, 5] = -448.0
+    ids = np.array([5, 0, 3, 8, 1, 2], dtype=np.int32)
+    valid = np.array([16, 16, 16, 16, 16, 11], dtype=np.int32)
+    k_o, v_o = ref.new_pool(nb, hkv, d, "e4m3")
+    s_o = np.ones((2, nb, hkv), dtype=np.float32)
+    ref.kv_cache_write_e4m3_blocks(k_o, v_o, s_o, xk, xv, ids, valid)
+    assert np.all(s_o[:, ids] == 1.0)
+    k = torch.full((nb, hkv, 16 * d), 0x7F, dtype=torch.uint8, device="cuda")
+    v = torch.full_like(k, 0x7F)
+    sc = torch.ones((2, nb, hkv), dtype=torch.float32, device="cuda")
+    abi.kv_cache_quantize_e4m3(torch.from_numpy(xk).cuda(), torch.from_numpy(xv).cuda(),
+                               torch.from_numpy(ids).cuda(), torch.from_numpy(valid).cuda(), k, v, sc)
+    torch.cuda.synchronize()
+    assert np.array_equal(k.cpu().numpy(), k_o)
+    assert np.array_equal(v.cpu().numpy(), v_o)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+
+
 def test_fp8_attention_on_oracle_codes():
     """The FP8 kernel fed the oracle's own codes and scales (uploaded)."""
     _announce("fp8 oracle codes")
