@@ -91,7 +91,7 @@ SPECS = {
     "smollm2_360m": WorkloadSpec("smollm2_360m", 1002, 16, 15, 5, 64, "f16", "f16",
                                  ("uniform", 64, 2048), partition_size=256),
     "qwen25_1p5b": WorkloadSpec("qwen25_1p5b", 1003, 32, 12, 2, 128, "f16", "f16",
-                                ("uniform", 512, 4096), new_token_write=True, partition_size=384),
+                                ("uniform", 512, 4096), new_token_write=True, partition_size=768),
     "qwen25_7b_prefix": WorkloadSpec("qwen25_7b_prefix", 1004, 128, 28, 4, 128, "bf16", "bf16",
                                      ("lognormal", 1024, 1.0, 16, 32768), prefix_group=8,
                                      prefix_blocks=32, partition_size=768),
