@@ -146,6 +146,34 @@ def test_quantize_e4m3_rounding_boundaries():
     assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
 
 
+@pytest.mark.parametrize("hkv,d", [(4, 128), (3, 64)])
+def test_quantize_e4m3_valid_token_edge_cases(hkv, d):
+    """valid_tokens of 0, negative, 1, 15, 16 and above 16: the read window
+    of each (block, kv head) tile ends at its last valid row, so an empty
+    block reads nothing (codes 0, scale 1) and counts past 16 read all 16."""
+    from paged_kv_gqa_cache_amd import abi
+    _announce("quantize valid edges", hkv, d)
+    rng = np.random.default_rng(23)
+    valid = np.array([0, -3, 1, 15, 16, 40, 7, 0], dtype=np.int32)
+    n, nb = len(valid), 11
+    xk = rng.standard_normal((n, 16, hkv, d)).astype(np.float32) * 3
+    xv = rng.standard_normal((n, 16, hkv, d)).astype(np.float32)
+    ids = np.array([10, 0, 4, 2, 9, 5, 1, 7], dtype=np.int32)
+    k_o, v_o = ref.new_pool(nb, hkv, d, "e4m3")
+    s_o = np.full((2, nb, hkv), 5.0, dtype=np.float32)
+    ref.kv_cache_write_e4m3_blocks(k_o, v_o, s_o, xk, xv, ids, valid)
+    k = torch.full((nb, hkv, 16 * d), 0x7F, dtype=torch.uint8, device="cuda")
+    v = torch.full_like(k, 0x7F)
+    sc = torch.full((2, nb, hkv), 5.0, dtype=torch.float32, device="cuda")
+    abi.kv_cache_quantize_e4m3(torch.from_numpy(xk).cuda(), torch.from_numpy(xv).cuda(),
+                               torch.from_numpy(ids).cuda(), torch.from_numpy(valid).cuda(), k, v, sc)
+    torch.cuda.synchronize()
+    assert np.all(s_o[:, ids[valid <= 0]] == 1.0) and np.all(k_o[ids[valid <= 0]] == 0)
+    assert np.array_equal(k.cpu().numpy(), k_o)
+    assert np.array_equal(v.cpu().numpy(), v_o)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+
+
 def test_fp8_attention_on_oracle_codes():
     """The FP8 kernel fed the oracle's own codes and scales (uploaded)."""
     _announce("fp8 oracle codes")
