@@ -42,19 +42,21 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const WriteParams p) {
   const int64_t th = gid / chunks;
   const int h = static_cast<int>(th % p.num_kv_heads);
   const int64_t t = th / p.num_kv_heads;
+  // The token's K and V do not depend on its slot: their loads go out
+  // together with the slot's, so the launch waits for one round trip.
+  const size_t row_bytes = static_cast<size_t>(p.head_dim) * E;
+  const size_t src = (static_cast<size_t>(t) * p.num_kv_heads + h) * row_bytes + c * 16;
+  const u32x4 kv = ld16(static_cast<const char*>(p.k) + src);
+  const u32x4 vv = ld16(static_cast<const char*>(p.v) + src);
+  asm volatile("" ::: "memory");   // keeps the loads above the slot test (no wait is implied)
   const int64_t slot = p.slots[t];
   if (slot < 0 || slot >= static_cast<int64_t>(p.num_blocks) * kBlockSize) return;
   const int64_t blk = slot / kBlockSize;
   const int off = static_cast<int>(slot % kBlockSize);
-
-  const size_t row_bytes = static_cast<size_t>(p.head_dim) * E;
-  const size_t src = (static_cast<size_t>(t) * p.num_kv_heads + h) * row_bytes + c * 16;
   const size_t tile = (static_cast<size_t>(blk) * p.num_kv_heads + h) * kBlockSize * row_bytes;
 
-  const u32x4 kv = ld16(static_cast<const char*>(p.k) + src);
   st16(static_cast<char*>(p.k_cache) + tile + (static_cast<size_t>(c) * kBlockSize + off) * 16, kv);
 
-  const u32x4 vv = ld16(static_cast<const char*>(p.v) + src);
   Elem vals[X];
   __builtin_memcpy(vals, &vv, 16);
   Elem* vt = reinterpret_cast<Elem*>(static_cast<char*>(p.v_cache) + tile);
@@ -165,11 +167,11 @@ __global__ __launch_bounds__(128) void append_e4m3_kernel(const AppendParams p) 
   const bool is_v = blockIdx.z != 0;
   const int d = threadIdx.x;
   const int D = p.head_dim;
+  const float x = (is_v ? p.v : p.k)[(static_cast<size_t>(t) * p.num_kv_heads + h) * D + d];   // before the slot: one round trip
   const int64_t slot = p.slots[t];
   if (slot < 0 || slot >= static_cast<int64_t>(p.num_blocks) * kBlockSize) return;   // whole workgroup
   const int64_t blk = slot / kBlockSize;
   const int off = static_cast<int>(slot % kBlockSize);
-  const float x = (is_v ? p.v : p.k)[(static_cast<size_t>(t) * p.num_kv_heads + h) * D + d];
 
   float amax = fabsf(x);
 #pragma unroll
