@@ -1,5 +1,5 @@
 """bench.py's host side (no GPU): the one-GPU contract, the latency
-statistics, and that the committed HBM-counter summary belongs to the
+statistics, and that the committed profiles and HBM-counter summary belong to the
 committed kernel sources (else the bench line's roofline.traffic is null)."""
 from __future__ import annotations
 
@@ -28,3 +28,17 @@ def test_committed_counters_match_the_kernel_sources():
     traffic = bench.counters_traffic(bench.HEADLINE, bench.source_digest())
     assert traffic is not None, "profiles/ counter summary was taken from other kernel sources"
     assert 250e6 < traffic < 400e6
+
+
+def test_every_committed_kernel_profile_names_the_current_sources():
+    """Each rocprofv3 summary under profiles/ records the kernel-source
+    digest it was taken from; all of them must be the current one."""
+    import glob
+    import re
+    digest = bench.source_digest()
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "*")))
+    assert paths
+    for path in paths:
+        text = open(path).read()
+        found = re.findall(r"\b[0-9a-f]{16}\b", text)
+        assert digest in found, f"{os.path.basename(path)} was taken from other kernel sources"
