@@ -125,18 +125,23 @@ def append_token(block_codes: np.ndarray, scale, offset: int, x: np.ndarray):
 
     The pages fix a scale per page and head but no append policy.  Reading
     taken (listed in the design doc): the block keeps the bulk quantiser's
-    invariant scale = fp32(amax / 448) over its tokens so far.  The token's
-    own s = fp32(amax(|x|) / 448); a block's first token sets the scale (1 if
-    s is 0); a later token with s above the current scale grows it to s, and
-    the block's earlier codes are re-encoded: value = fp32(decode(c) *
-    old scale), code = nearest-even E4M3 of clamp(fp32(value / s)).  The token
-    itself is then encoded against the (new) scale like the bulk quantiser.
-    Every rounding step is fp32, as on the GPU.
+    invariant scale = fp32(amax / 448) over its tokens so far, 1 while they
+    are all zero.  The token's own s = fp32(amax(|x|) / 448).  When the token
+    is the block's first, or every earlier code of the block is a zero
+    (0x00 or 0x80: the earlier tokens' amax is 0, since the token that set a
+    non-zero scale holds a code of magnitude 448), the token sets the scale
+    (1 if s is 0) and the earlier codes stay as they are.  Otherwise a token
+    with s above the current scale grows it to s, and the block's earlier
+    codes are re-encoded: value = fp32(decode(c) * old scale), code =
+    nearest-even E4M3 of clamp(fp32(value / s)).  The token itself is then
+    encoded against the (new) scale like the bulk quantiser.  Every rounding
+    step is fp32, as on the GPU.
     """
     codes = np.array(block_codes, dtype=np.uint8, copy=True)
     x = np.asarray(x, dtype=np.float32)
     s_tok = np.float32(np.max(np.abs(x))) / np.float32(E4M3_MAX)
-    if offset == 0:
+    earlier_zero = not np.any(codes[:offset] & 0x7F)   # vacuously true for the first token
+    if earlier_zero:
         s = s_tok if s_tok > 0 else np.float32(1)
     else:
         s = np.float32(scale)

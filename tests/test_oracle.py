@@ -335,6 +335,41 @@ def test_fp8_oracle_equals_sdpa_on_torch_dequantised_values():
         np.testing.assert_allclose(out8[b], o.numpy(), rtol=0, atol=1e-12)
 
 
+def test_unquantised_fp8_workload_oracle_equals_sdpa_on_the_fp32_values():
+    """The reference of the FP8 quantisation error: the oracle over an E4M3
+    workload's unquantised fp32 K/V (an f32 pool) equals float64 SDPA on the
+    generator's fp32 values read straight from its per-block arrays."""
+    from tests.helpers import oracle_pool_unquantised
+    w = small("qwen25_7b_fp8", num_seqs=3, lengths=("uniform", 1, 200))
+    k, v, _ = oracle_pool_unquantised(w)
+    out = ref.decode_attention(w.q, "f16", k, v, "f32", w.block_tables, w.context_lens, w.scale)
+    s = w.spec
+    q = torch.from_numpy(ref.to_f64(w.q, "f16"))
+    for b in range(s.num_seqs):
+        Ks, Vs = zip(*(logical_kv(w, b, h, dtype="f32") for h in range(s.num_kv_heads)))
+        K = torch.from_numpy(np.stack(Ks)).repeat_interleave(s.group_size, dim=0)
+        V = torch.from_numpy(np.stack(Vs)).repeat_interleave(s.group_size, dim=0)
+        o = torch.nn.functional.scaled_dot_product_attention(q[b][:, None, :], K, V, scale=w.scale)[:, 0, :]
+        np.testing.assert_allclose(out[b], o.numpy(), rtol=0, atol=1e-12)
+
+
+def test_fp8_quantisation_error_is_within_its_model():
+    """Mean |E4M3 oracle - unquantised oracle| on N(0,1) K/V: each E4M3 value
+    carries a relative error uniform in +-2^-4 (3 mantissa bits), so V's error
+    averages to about 0.036 * E|v| / sqrt(N_eff) over the softmax and K's
+    adds a comparable term; with N_eff ~ L / e for unit-variance logits the
+    figure sits near 0.06 / sqrt(L).  Pinned between a fifth of that and
+    three times it, so a dropped scale (error ~1) or an exact copy (0) fails."""
+    from tests.helpers import oracle_pool_unquantised
+    w = small("qwen25_7b_fp8", num_seqs=4, lengths=("fixed", 512))
+    o8 = run_oracle(w)
+    k, v, _ = oracle_pool_unquantised(w)
+    o32 = ref.decode_attention(w.q, "f16", k, v, "f32", w.block_tables, w.context_lens, w.scale)
+    mae = float(np.mean(np.abs(o8 - o32)))
+    model = 0.06 / math.sqrt(512)
+    assert model / 5 < mae < 3 * model, mae
+
+
 # -------------------------------------------------------------- generator ---
 
 def test_generator_is_deterministic_and_well_formed():
@@ -574,6 +609,42 @@ def test_append_scale_is_fp32_amax_over_448_and_error_is_bounded(seed):
 def test_append_of_a_zero_token_to_a_fresh_block_has_scale_one():
     codes, s = e4m3.append_token(np.full((16, 64), 0x55, np.uint8), np.float32(7), 0, np.zeros(64, np.float32))
     assert s == 1 and np.all(codes[0] == 0) and np.all(codes[1:] == 0x55)
+
+
+@pytest.mark.parametrize("lead_zeros", [1, 4])
+def test_append_after_all_zero_tokens_equals_the_bulk_quantiser(lead_zeros):
+    """A block whose first tokens are zero (scale 1, codes 0): the first
+    non-zero token sets the scale as the bulk quantiser would, even below
+    amax 448 (scale < 1), and with it the largest, the codes are the bulk
+    quantiser's too."""
+    x = _grow_free_block(n=12, seed=lead_zeros)
+    x[:lead_zeros] = 0
+    x[1:lead_zeros, :5] = np.float32(-0.0)
+    x[lead_zeros, 0] = np.float32(2.0) * np.max(np.abs(x))   # first non-zero token holds the amax
+    codes, s = np.zeros((16, 64), np.uint8), np.float32(0)
+    for t in range(len(x)):
+        codes, s = e4m3.append_token(codes, s, t, x[t])
+        if t < lead_zeros:
+            assert s == 1
+    blk = np.zeros((1, 16, 1, 64), np.float32)
+    blk[0, :len(x), 0] = x
+    bc, bs = e4m3.quantize_blocks(blk, np.array([len(x)]))
+    assert bs[0, 0] < 1 and s == bs[0, 0]
+    assert np.array_equal(codes[:len(x)], bc[0, :len(x), 0])
+
+
+@pytest.mark.parametrize("lead_zeros", [1, 3])
+def test_append_after_zero_tokens_keeps_scale_fp32_amax_over_448(lead_zeros):
+    """Zero tokens, then rising magnitudes: after every step the scale is
+    fp32(amax / 448) over the tokens so far (1 while they are all zero)."""
+    rng = np.random.default_rng(lead_zeros)
+    x = rng.standard_normal((16, 64), dtype=np.float32) * np.linspace(0.05, 2.0, 16, dtype=np.float32)[:, None]
+    x[:lead_zeros] = 0
+    codes, s = np.zeros((16, 64), np.uint8), np.float32(0)
+    for t in range(16):
+        codes, s = e4m3.append_token(codes, s, t, x[t])
+        amax = np.float32(np.max(np.abs(x[:t + 1])))
+        assert s == (amax / np.float32(448) if amax > 0 else 1)
 
 
 def test_pool_append_matches_per_head_steps_and_leaves_other_slots():
