@@ -101,7 +101,7 @@ def source_digest() -> str:
 def counters_traffic(workload: str, digest: str):
     """HBM bytes per partial-kernel launch from the committed rocprofv3 counter
     summary, if it was taken from the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"paged_decode_partial_{workload}_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"paged_decode_{workload}_hbm_counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -213,35 +213,96 @@ class Runner:
         return wall / steps, kernel_ms
 
 
-def cpu_baseline(name: str):
-    """The float64 oracle on this host, one thread, on the full batch."""
+def host_cores() -> int:
+    """Cores this process may run on, capped by OMP_NUM_THREADS when set (a
+    one-GPU machine exports its CPU share there)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+    except ValueError:
+        pass
+    return max(1, n)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+_CPU_STATE = {}
+
+
+def _oracle_chunk(bounds):
+    """One worker's share of a decode step: the oracle over sequences
+    [b0, b1) of the workload the parent process set up before forking."""
+    from oracle import paged_attention as ref
+    w, k, v, sc = _CPU_STATE["w"], _CPU_STATE["k"], _CPU_STATE["v"], _CPU_STATE["sc"]
+    b0, b1 = bounds
+    s = w.spec
+    if w.new_slots is not None:
+        ref.kv_cache_write(k, v, w.new_k[b0:b1], w.new_v[b0:b1], w.new_slots[b0:b1], s.kv_dtype)
+    ref.decode_attention(w.q[b0:b1], s.q_dtype, k, v, s.kv_dtype, w.block_tables[b0:b1],
+                         w.context_lens[b0:b1], w.scale, sc, window=s.window)
+    return b1 - b0
+
+
+def cpu_baseline_child(name: str) -> dict:
+    """The float64 oracle on this host's cores, on the full batch: the
+    sequences are dealt to one forked worker process per core (each with
+    one BLAS thread), and a step is the wall time until every worker has
+    finished its sequences (the new-token write included).  Runs in a
+    child process of bench.py that never touches the GPU."""
+    import multiprocessing as mp
+
     import numpy as np
     from threadpoolctl import threadpool_limits
 
-    from oracle import paged_attention as ref
     from paged_kv_gqa_cache_amd import workloads
     from tests.helpers import oracle_pool
 
     w = workloads.generate(name)
     k, v, sc = oracle_pool(w)
-    s = w.spec
+    _CPU_STATE.update(w=w, k=k, v=v, sc=sc)
+    cores = host_cores()
+    B = w.spec.num_seqs
+    # One task per sequence, longest first, handed to whichever worker is
+    # free, so the workers' loads are even (the oracle's cost is linear in
+    # the context).
+    order = np.argsort(-w.context_lens.astype(np.int64), kind="stable")
+    chunks = [(int(b), int(b) + 1) for b in order]
     times = []
-    with threadpool_limits(1):
-        # Whole decode steps until about 10 s of CPU work (at least 3 steps).
+    with threadpool_limits(1), mp.get_context("fork").Pool(cores) as pool:
+        pool.map(_oracle_chunk, chunks[:cores])   # workers started and warm
         t_all = time.perf_counter()
-        while len(times) < 3 or (time.perf_counter() - t_all < 10.0 and len(times) < 50):
+        while len(times) < 3 or (time.perf_counter() - t_all < 15.0 and len(times) < 1000):
             t = time.perf_counter()
-            if w.new_slots is not None:
-                ref.kv_cache_write(k, v, w.new_k, w.new_v, w.new_slots, s.kv_dtype)
-            ref.decode_attention(w.q, s.q_dtype, k, v, s.kv_dtype, w.block_tables, w.context_lens,
-                                 w.scale, sc)
+            done = sum(pool.map(_oracle_chunk, chunks, chunksize=1))
             times.append(time.perf_counter() - t)
+            assert done == B
     t = float(np.median(times))
-    return {"value": round(workloads.kv_bytes(w, unique=True) / t / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"the full {s.num_seqs}-sequence batch of the headline workload, one decode step "
-                      f"(gather + softmax + PV in float64, numpy, 1 BLAS thread), repeated {len(times)} "
-                      f"times (~{sum(times):.0f} s); median {t * 1e3:.0f} ms per step"}
+    return {"value": round(workloads.kv_bytes(w, unique=True) / t / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
+            "us_per_step": round(t * 1e6, 1), "seqs_layers_per_s": round(B / t, 1),
+            "sample": f"the full {B}-sequence batch of the headline workload, one decode step per sample "
+                      f"(gather + softmax + PV in float64 numpy), sequences dealt to {cores} forked worker "
+                      f"processes with one BLAS thread each; {len(times)} steps (~{sum(times):.0f} s), "
+                      f"median {t * 1e3:.0f} ms per step"}
+
+
+def cpu_baseline(name: str) -> dict:
+    """Runs cpu_baseline_child in a fresh child process (this process has
+    the GPU open; the child only uses the host) and returns its record."""
+    import subprocess
+    res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--workload", name],
+                         capture_output=True, text=True, cwd=ROOT, timeout=600)
+    if res.returncode != 0:
+        raise RuntimeError(f"cpu baseline child failed ({res.returncode}): {res.stderr[-2000:]}")
+    return json.loads(res.stdout.strip().splitlines()[-1])
 
 
 def time_calls(fn, n: int, warmup: int = 3) -> float:
@@ -319,7 +380,43 @@ def torch_materialising(r, steps: int) -> dict:
                     "matmul (context for the materialising-reference comparison; not part of the path)"}
 
 
-ROW_NAMES = ("single_pass", "fp8_e4m3_decode", "e4m3_bulk_quantise", "e4m3_append", "sliding_window",
+def unquantised_reference(w, seq_chunk: int = 16):
+    """float64 [B, Hq, D] attention of an E4M3 workload over its K/V before
+    quantisation (the generator's float32 values), computed in plain
+    PyTorch float64 on the GPU: each sequence's blocks gathered to dense K/V
+    from the generator's per-block arrays, then softmax(q K^T * scale) V
+    with the same fp16 q.  The reference for the FP8 row's mean absolute
+    error (quantisation error, not a parity gate); not part of the path."""
+    import numpy as np
+    import torch
+    s = w.spec
+    B, Hq, Hkv, D = s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim
+    G = Hq // Hkv
+    L = w.context_lens.astype(np.int64)
+    nb = (L + 15) // 16
+    where = np.full(w.num_blocks, -1, np.int64)
+    where[w.fill_blocks] = np.arange(len(w.fill_blocks))
+    kf = torch.from_numpy(w.fill_k.view(np.float32)).cuda()   # [n, 16, Hkv, D]
+    vf = torch.from_numpy(w.fill_v.view(np.float32)).cuda()
+    q = torch.from_numpy(w.q.view(np.float16)).cuda().double().view(B, Hkv, G, D)
+    out = torch.empty((B, Hq, D), dtype=torch.float64, device="cuda")
+    for b0 in range(0, B, seq_chunk):
+        b1 = min(B, b0 + seq_chunk)
+        m = int(nb[b0:b1].max())
+        idx = np.zeros((b1 - b0, m), np.int64)
+        for i, b in enumerate(range(b0, b1)):
+            idx[i, :nb[b]] = where[w.block_tables[b, :nb[b]]]
+        ix = torch.from_numpy(idx).cuda()
+        K = kf[ix].double().permute(0, 3, 1, 2, 4).reshape(b1 - b0, Hkv, m * 16, D)
+        V = vf[ix].double().permute(0, 3, 1, 2, 4).reshape(b1 - b0, Hkv, m * 16, D).contiguous()
+        keep = torch.arange(m * 16, device="cuda")[None, :] < torch.from_numpy(L[b0:b1]).cuda()[:, None]
+        S = torch.matmul(q[b0:b1], K.transpose(-1, -2).contiguous()) * w.scale
+        S = S.masked_fill(~keep[:, None, None, :], float("-inf"))
+        out[b0:b1] = torch.matmul(torch.softmax(S, dim=-1), V).reshape(b1 - b0, Hq, D)
+    return out
+
+
+ROW_NAMES = ("tiny_layer", "smollm2_layer", "single_pass", "fp8_e4m3_decode", "e4m3_bulk_quantise", "e4m3_append", "sliding_window",
              "chunked_prefill", "spec_verify_4", "copy_blocks", "kv_slot_write")
 
 
@@ -336,6 +433,23 @@ def measure_rows(args, only=None) -> dict:
     rows = {}
     steps, warm = max(10, args.steps // 2), max(3, args.warmup // 2)
     want = (lambda k: True) if not only else (lambda k: k in only)
+
+    # The two small layers (tiny: 4 fp32 sequences with their new-token
+    # write; SmolLM2-360M-shaped: 16 fp16 sequences): launch-bound, reported
+    # for the us/step and sequences x layers/s figures.
+    for key, name, path in (("tiny_layer", "tiny", "step"), ("smollm2_layer", "smollm2_360m", "pair")):
+        if not want(key):
+            continue
+        r = Runner(name, args.layers, None, path)
+        t, part = r.run(steps, warm)
+        ms = sum(part) / len(part)
+        row = hbm_row(r.unique_bytes, ms, "unique K/V bytes read per step")
+        row.update({"workload": f"{name}: {DESCRIPTIONS[name]}", "path": path, "partition_size": r.P,
+                    "us_per_step": round(t * 1e6, 2), "step_GBps": round(r.unique_bytes / t / 1e9, 1),
+                    "seqs_layers_per_s": round(r.spec.num_seqs / t, 1)})
+        rows[key] = row
+        del r
+        torch.cuda.empty_cache()
 
     # The headline layer through the single-pass entry point (no workspace,
     # one work item per sequence and kv head: the longest context bounds it).
@@ -372,6 +486,16 @@ def measure_rows(args, only=None) -> dict:
             row = hbm_row(r.unique_bytes, ms, "unique K/V (+ E4M3 scales) bytes read per step")
             row.update({"workload": f"{name}: {DESCRIPTIONS[name]}", "path": path,
                         "us_per_step": round(t * 1e6, 2), "step_GBps": round(r.unique_bytes / t / 1e9, 1)})
+            if name == "qwen25_7b_fp8":
+                # Quantisation error of the FP8 path: its fp32 output against
+                # attention over the unquantised fp32 K/V (same fp16 q).
+                k, v, sc = r.pools[0]
+                ours = abi.paged_decode_attention_balanced(r.q, k, v, r.tables, r.lens, r.w.scale, sc, r.bws,
+                                                           out_dtype=torch.float32).double()
+                d = (ours - unquantised_reference(r.w)).abs()
+                row.update({"mae_vs_fp32": float(d.mean()), "max_abs_vs_fp32": float(d.max()),
+                            "mae_is": "mean over all B x Hq x D outputs of |FP8 path (fp32 out) - attention over "
+                                      "the unquantised fp32 K/V with the same fp16 q (float64)|"})
             rows[key] = row
         if name == "qwen25_7b_fp8":
             # Bulk quantiser on the same layer: fp32 blocks in, codes + scales out.
@@ -549,7 +673,12 @@ def main():
                     help="path for the B=32 line (its fastest: the fused step, write and attention in one launch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 256 MiB device to device (reference kernel for HBM counters)")
+    ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+
+    if args.cpu_baseline_child:   # host only: never touches the GPU
+        print(json.dumps(cpu_baseline_child(args.workload)), flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -586,11 +715,22 @@ def main():
     if not args.no_secondary and args.workload != SECONDARY:
         r2 = Runner(SECONDARY, args.layers, None, args.secondary_path)
         t2, p2 = r2.run(args.steps, args.warmup)
+        k2 = sum(p2) / len(p2)
         b32 = {"workload": f"{SECONDARY}: {DESCRIPTIONS[SECONDARY]}", "path": args.secondary_path,
                "partition_size": r2.P, "us_per_step": round(t2 * 1e6, 2),
-               "dominant_kernel_us": round(sum(p2) / len(p2) * 1e3, 2),
+               "dominant_kernel_us": round(k2 * 1e3, 2),
                "kv_GBps": round(r2.unique_bytes / t2 / 1e9, 1),
-               "seqs_layers_per_s": round(r2.spec.num_seqs / t2, 1)}
+               "seqs_layers_per_s": round(r2.spec.num_seqs / t2, 1),
+               "roofline": {"bound": "hbm", "achieved": round(r2.unique_bytes / (k2 * 1e-3) / 1e9, 1),
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(r2.unique_bytes / (k2 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                            "bytes": r2.unique_bytes,
+                            "bytes_are": "unique K/V bytes read per step (the 32 new tokens' writes excluded)",
+                            "kernel": {"pair": "paged_decode_persistent, split partial mode",
+                                       "fused": "paged_decode_persistent, split mode with in-kernel merge",
+                                       "balanced": "paged_decode_stream + stream_merge_kernel",
+                                       "step": "paged_decode_persistent, split mode with the new-token write "
+                                               "and in-kernel merge"}[args.secondary_path]}}
         del r2
 
     torch_ref = None

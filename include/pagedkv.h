@@ -56,6 +56,11 @@
  *        (groups of 4 consecutive tokens of one dim are adjacent).
  *   Both place each 64-lane wave's 16-byte loads on one contiguous 1 KiB and
  *   hand the matrix cores their operands without a transpose.
+ *   This byte layout is the library's own, not a [NB][Hkv][16][D] array:
+ *   callers fill a pool only through the library's writers (kv_cache_write,
+ *   paged_decode_step, kv_cache_quantize_e4m3, kv_cache_append_e4m3,
+ *   kv_cache_copy_blocks) and treat the tiles as opaque.  Only the sizes
+ *   above are part of the contract: NB * Hkv * 16 * D elements per cache.
  *
  * Supported combinations (q / KV / out): f32/f32/f32; f16/f16/{f32,f16};
  * bf16/bf16/{f32,bf16}; f16/e4m3/{f32,f16}.  D in {64, 128}, G in 1..16,
@@ -393,6 +398,12 @@ const char* pkv_last_error(void);
 
 /* Library version string.  */
 const char* pkv_version(void);
+
+/* The same two helpers under the library's own prefix: pagedkv_last_error
+ * returns exactly what pkv_last_error returns, pagedkv_version what
+ * pkv_version returns.  */
+const char* pagedkv_last_error(void);
+const char* pagedkv_version(void);
 
 /*
  * pkv_read_bandwidth_probe - a measurement aid, not part of the attention

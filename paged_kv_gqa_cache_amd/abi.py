@@ -67,6 +67,8 @@ def _load():
         "paged_decode_workspace_bytes": (ctypes.c_int64, [D, I32]),
         "pkv_last_error": (ctypes.c_char_p, []),
         "pkv_version": (ctypes.c_char_p, []),
+        "pagedkv_last_error": (ctypes.c_char_p, []),
+        "pagedkv_version": (ctypes.c_char_p, []),
         "pkv_read_bandwidth_probe": (ctypes.c_int, [P, I64, P, I32, P]),
     }
     for name, (res, args) in sigs.items():
@@ -83,7 +85,7 @@ EXPORTED = ("kv_cache_write", "kv_cache_quantize_e4m3", "kv_cache_append_e4m3", 
             "paged_decode_attention_balanced", "paged_decode_balanced_workspace_bytes",
             "paged_prefill_attention", "paged_prefill_workspace_bytes",
             "paged_decode_num_partitions", "paged_decode_workspace_bytes", "pkv_last_error",
-            "pkv_version", "pkv_read_bandwidth_probe")
+            "pkv_version", "pagedkv_last_error", "pagedkv_version", "pkv_read_bandwidth_probe")
 
 
 def lib():

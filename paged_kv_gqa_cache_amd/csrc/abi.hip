@@ -154,7 +154,11 @@ extern "C" {
 
 const char* pkv_last_error(void) { return g_err; }
 
-const char* pkv_version(void) { return "pagedkv 0.1.0 gfx950"; }
+const char* pkv_version(void) { return "pagedkv 0.2.0 gfx950"; }
+
+const char* pagedkv_last_error(void) { return g_err; }
+
+const char* pagedkv_version(void) { return pkv_version(); }
 
 int pkv_read_bandwidth_probe(const void* src, int64_t bytes, uint32_t* out, int32_t out_words, void* stream) {
   if (!src || !out) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");

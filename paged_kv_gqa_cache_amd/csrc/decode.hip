@@ -37,7 +37,8 @@
 //    multi-token step, when it has many rows per sequence, takes tiles in
 //    pairs and runs PV on the K = 32 form (twice the rate of K = 16).
 //  * E4M3 codes decode to fp16 exactly with the packed hardware conversion;
-//    the block's K scale folds into its logit factor, its V scale into P.
+//    the block's K scale folds into its logit factor, its V scale into P
+//    (times a running power of two that keeps P inside f16's range).
 //  * Softmax runs in base 2 (log2 e folded into the scale).
 #include "pkv_common.h"
 #include "pkv_launch.h"
@@ -211,14 +212,22 @@ template <int D> struct TileOps<KV_E4M3, D> {
       vt[m].x &= mk; vt[m].y &= mk; vt[m].z &= mk; vt[m].w &= mk;
     }
   }
-  // pscale = V scale * 2^8: P * pscale stays well inside f16's range for the
-  // hi/lo split; the accumulator carries the 2^8, which kOutScale removes.
-  static constexpr float kOutScale = 1.f / 256.f;
+  // pscale = the block's V scale times a power of two chosen by the caller
+  // (attend_packs) so that P * pscale stays inside f16's range for the hi/lo
+  // split whatever the scale; the caller removes the power of two at the end.
   __device__ static void pv(f32x4 (&o)[NT], const u32x4 (&vt)[NLOAD], const float (&p)[4], float pscale) {
+    // hi + lo must split one fp32 value ps exactly.  Left to itself the
+    // compiler derives the hi that lo is taken against straight from the
+    // unrounded product p * pscale (a mixed-precision multiply with one f16
+    // rounding) while the hi fed to the matrix cores rounds the fp32
+    // product; where those two differ the pair is off by one f16 ulp of ps
+    // (2^-11 relative).  Passing the product through an opaque copy makes
+    // both come from the same fp32 register.
+#pragma clang fp contract(off)
     f16x4 hi, lo;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float ps = p[j] * pscale;
+      const float ps = __uint_as_float(opaque_copy(__float_as_uint(p[j] * pscale)));
       const _Float16 h = static_cast<_Float16>(ps);
       hi[j] = h;
       lo[j] = static_cast<_Float16>(ps - static_cast<float>(h));
@@ -472,6 +481,15 @@ __device__ __forceinline__ void attend_packs(const DecodeParams& p, int b, int h
     for (int m = 0; m < NL; ++m) vt[m] = buffer_ld16_policy<POLICY>(vr, lane_off[m]);
   };
 
+  // E4M3 V scales: P goes to the matrix cores as p * vsc * 2^(7 - vexp),
+  // where 2^vexp bounds every V scale seen so far (vexp is wave-uniform: a
+  // scale belongs to one (block, kv head), the same for every lane).  With
+  // p <= 2^kSlack = 2^8 the product stays below 2^15, inside f16's range,
+  // for any scale; a block whose scale needs a larger vexp shrinks the
+  // accumulators by the (exact) power of two first, and the end of the run
+  // multiplies them by 2^(vexp - 7).
+  int vexp = -126;
+
   // Lowest causal limit of each pack (wave-uniform: lane 0 holds the pack's
   // first token, the smallest limit); blocks that end at or before it need
   // no causal mask.
@@ -485,7 +503,17 @@ __device__ __forceinline__ void attend_packs(const DecodeParams& p, int b, int h
     float pscale = 1.f;
     if constexpr (KVT == KV_E4M3) {
       f *= ksc;
-      pscale = 256.f * vsc;
+      const uint32_t vbits = __builtin_amdgcn_readfirstlane(__float_as_uint(vsc));
+      const int e_blk = static_cast<int>((vbits >> 23) & 0xFFu) - 126;   // vsc < 2^e_blk
+      if (e_blk > vexp) {
+        const float shrink = __builtin_amdgcn_ldexpf(1.f, vexp - e_blk);
+#pragma unroll
+        for (int k = 0; k < NPK; ++k)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) st[k].o[n] *= shrink;
+        vexp = e_blk;
+      }
+      pscale = __builtin_amdgcn_ldexpf(__uint_as_float(vbits), 7 - vexp);
     }
     const bool tail = tok0 + kBlockSize > L;   // the sequence's last, partly filled block
     if (tail) T::mask_v(vt, L - tok0 - 4 * g);
@@ -653,10 +681,11 @@ __device__ __forceinline__ void attend_packs(const DecodeParams& p, int b, int h
     }
   }
   if constexpr (KVT == KV_E4M3) {
+    const float grow = __builtin_amdgcn_ldexpf(1.f, vexp - 7);
 #pragma unroll
     for (int k = 0; k < NPK; ++k)
 #pragma unroll
-      for (int n = 0; n < NT; ++n) st[k].o[n] *= T::kOutScale;
+      for (int n = 0; n < NT; ++n) st[k].o[n] *= grow;
   }
 }
 

@@ -157,10 +157,13 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const QuantParams p)
 
 // One workgroup (D threads) per (token, kv head, K-or-V); thread d owns dim
 // d of every slot of the block.  Each rounding step is fp32: token scale
-// s = amax / 448; a block's first token sets the scale (1 if s is 0); a
-// later token with s above the stored scale re-encodes the earlier slots as
-// code(clamp(decode(c) * old / s)) and stores s; the token's own code is
-// code(clamp(x / scale)).  At most one token per block per launch.
+// s = amax / 448.  When every earlier code of the block is a zero (always so
+// for its first token), the token sets the scale (1 if s is 0): the block's
+// tokens so far have amax 0, and the scale follows the bulk quantiser's
+// rule.  Otherwise a token with s above the stored scale re-encodes the
+// earlier slots as code(clamp(decode(c) * old / s)) and stores s.  The
+// token's own code is code(clamp(x / scale)).  At most one token per block
+// per launch.
 __global__ __launch_bounds__(128) void append_e4m3_kernel(const AppendParams p) {
   const int t = blockIdx.x;
   const int h = blockIdx.y;
@@ -190,8 +193,12 @@ __global__ __launch_bounds__(128) void append_e4m3_kernel(const AppendParams p) 
   };
   float* sc = p.kv_scales + (is_v ? static_cast<size_t>(p.num_blocks) * p.num_kv_heads : 0) +
               static_cast<size_t>(blk) * p.num_kv_heads + h;
+  // Any non-zero code (magnitude bits) among this dim's earlier slots.
+  uint32_t nz = 0;
+  for (int o = 0; o < off; ++o) nz |= tile[pos(o)] & 0x7Fu;
+  const bool earlier_zero = __syncthreads_or(static_cast<int>(nz)) == 0;
   float s;
-  if (off == 0) {
+  if (earlier_zero) {
     s = s_tok > 0.f ? s_tok : 1.0f;
   } else {
     const float s_old = *sc;
