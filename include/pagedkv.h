@@ -350,6 +350,26 @@ int paged_decode_attention_balanced(const void* q, const void* k_cache, const vo
 int64_t paged_decode_balanced_workspace_bytes(const pkv_desc* desc);
 
 /*
+ * paged_decode_attention_balanced_static - paged_decode_attention_balanced
+ * without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  It allocates nothing and calls no allocating routine;
+ * its partials live in a 32 MiB device array inside the library, one copy
+ * per GPU, held until the process ends (looked up on the first call on each
+ * device, which must be the current device).  Same arguments, kernels and
+ * result as paged_decode_attention_balanced.  Problems needing more than
+ * 32 MiB of workspace (paged_decode_balanced_workspace_bytes) return
+ * PKV_ERR_INVALID_ARG.  The array keeps the last call's contents and needs no
+ * clearing (every byte is written before it is read within a call); calls
+ * that overlap in time on one GPU (different streams, or different threads)
+ * share it and race: serialise them.
+ */
+int paged_decode_attention_balanced_static(const void* q, const void* k_cache, const void* v_cache,
+                                           const int32_t* block_tables, const int32_t* context_lens,
+                                           float scale, const float* kv_scales, void* out,
+                                           const pkv_desc* desc, void* stream);
+
+/*
  * paged_prefill_attention - attention for several new tokens per sequence
  * (chunked prefill, speculative verification), causal inside the new
  * tokens ("rvLLM: High-performance LLM inference in Rust", section "CUDA

@@ -61,6 +61,7 @@ def _load():
         "paged_decode_step": (ctypes.c_int, [P, P, P, P, P, P, P, F, I32, P, I64, P, D, P]),
         "paged_decode_attention_balanced": (ctypes.c_int, [P, P, P, P, P, F, P, P, I64, P, D, P]),
         "paged_decode_balanced_workspace_bytes": (ctypes.c_int64, [D]),
+        "paged_decode_attention_balanced_static": (ctypes.c_int, [P, P, P, P, P, F, P, P, D, P]),
         "paged_prefill_attention": (ctypes.c_int, [P, P, P, P, P, P, I32, F, P, I32, P, I64, P, D, P]),
         "paged_prefill_workspace_bytes": (ctypes.c_int64, [D, I32, I32]),
         "paged_decode_num_partitions": (ctypes.c_int64, [D, I32]),
@@ -83,6 +84,7 @@ EXPORTED = ("kv_cache_write", "kv_cache_quantize_e4m3", "kv_cache_append_e4m3", 
             "paged_decode_attention_partial", "paged_decode_attention_reduce",
             "paged_decode_attention_split", "paged_decode_split_workspace_bytes", "paged_decode_step",
             "paged_decode_attention_balanced", "paged_decode_balanced_workspace_bytes",
+            "paged_decode_attention_balanced_static",
             "paged_prefill_attention", "paged_prefill_workspace_bytes",
             "paged_decode_num_partitions", "paged_decode_workspace_bytes", "pkv_last_error",
             "pkv_version", "pagedkv_last_error", "pagedkv_version", "pkv_read_bandwidth_probe")
@@ -291,6 +293,20 @@ def paged_decode_attention_balanced(q, k_cache, v_cache, block_tables, context_l
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         float(scale), _ptr(kv_scales), _ptr(workspace), workspace.numel(),
         _ptr(out), ctypes.byref(desc), _stream(stream)))
+    return out
+
+
+def paged_decode_attention_balanced_static(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales,
+                                           out=None, out_dtype=None, stream=None, window=0):
+    """paged_decode_attention_balanced with the library's static scratch
+    instead of a workspace (no device allocation by the library; ``out`` is
+    allocated here only when not given)."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    desc = _attn_desc(q, k_cache, block_tables, _code(out), window)
+    _check("paged_decode_attention_balanced_static", _lib.paged_decode_attention_balanced_static(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        float(scale), _ptr(kv_scales), _ptr(out), ctypes.byref(desc), _stream(stream)))
     return out
 
 

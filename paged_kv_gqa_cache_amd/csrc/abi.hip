@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "../../include/pagedkv.h"
 #include "pkv_launch.h"
@@ -146,6 +147,37 @@ pkv::DecodeParams decode_params(const void* q, const void* kc, const void* vc, c
   p.out_dtype = d->out_dtype;
   p.window = d->sliding_window;
   return p;
+}
+
+// Scratch of paged_decode_attention_balanced_static: a file-scope device
+// array (one copy on every GPU the library runs on, held until the process
+// ends).  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is ever handed to a kernel.
+constexpr int64_t kStaticScratchBytes = int64_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on its first use on
+// that device (the device is current for the lookup).
+int static_scratch(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_UNSUPPORTED, "device %d past the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return PKV_OK;
 }
 
 }  // namespace
@@ -390,25 +422,25 @@ int paged_decode_step(const void* q, const void* k_new, const void* v_new, void*
                       partition_size, workspace, workspace_bytes, out, desc, stream, "paged_decode_step launch");
 }
 
-int paged_decode_attention_balanced(const void* q, const void* k_cache, const void* v_cache,
-                                    const int32_t* block_tables, const int32_t* context_lens, float scale,
-                                    const float* kv_scales, void* workspace, int64_t workspace_bytes,
-                                    void* out, const pkv_desc* desc, void* stream) {
+// Checks shared by the two balanced entry points (everything but the workspace).
+static int balanced_checks(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, float scale, const float* kv_scales, const void* out,
+                           const pkv_desc* desc) {
   if (int e = check_desc(desc, true)) return e;
   if (int e = check_attn_types(desc, kv_scales)) return e;
   if (int e = check_balanced(desc)) return e;
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
-  if (desc->num_seqs == 0) return ok();
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !workspace || !out)
+  if (desc->num_seqs == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
-  if (reinterpret_cast<uintptr_t>(workspace) % 256)
-    return fail(PKV_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-  const BalancedLayout lay = balanced_layout(desc);
-  if (workspace_bytes < lay.total)
-    return fail(PKV_ERR_INVALID_ARG, "workspace of %lld bytes is smaller than the %lld needed",
-                static_cast<long long>(workspace_bytes), static_cast<long long>(lay.total));
-  if (lay.slots > 0x7FFFFFFF / 16) return fail(PKV_ERR_INVALID_ARG, "too many partial slots");
-  char* ws = static_cast<char*>(workspace);
+  return PKV_OK;
+}
+
+// The balanced schedule's two launches on a workspace already checked
+// against lay.
+static int balanced_run(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                        const int32_t* context_lens, float scale, const float* kv_scales, char* ws,
+                        const BalancedLayout& lay, void* out, const pkv_desc* desc, void* stream, const char* what) {
   pkv::DecodeParams p = decode_params(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales, desc);
   p.out = out;
   p.seq_tiles = reinterpret_cast<int32_t*>(ws);
@@ -417,9 +449,7 @@ int paged_decode_attention_balanced(const void* q, const void* k_cache, const vo
   p.num_workers = lay.workers;
   p.num_slots = static_cast<int32_t>(lay.slots);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (int e = hip_status(pkv::launch_stream(p, desc->kv_dtype, desc->head_dim, st),
-                         "paged_decode_attention_balanced launch"))
-    return e;
+  if (int e = hip_status(pkv::launch_stream(p, desc->kv_dtype, desc->head_dim, st), what)) return e;
   pkv::ReduceParams r{};
   r.tmp_out = p.tmp_out;
   r.tmp_lse = p.tmp_lse;
@@ -435,7 +465,42 @@ int paged_decode_attention_balanced(const void* q, const void* k_cache, const vo
   r.num_workers = p.num_workers;
   r.num_slots = p.num_slots;
   r.window = p.window;
-  return hip_status(pkv::launch_stream_merge(r, st), "paged_decode_attention_balanced merge launch");
+  return hip_status(pkv::launch_stream_merge(r, st), what);
+}
+
+int paged_decode_attention_balanced(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                    const float* kv_scales, void* workspace, int64_t workspace_bytes,
+                                    void* out, const pkv_desc* desc, void* stream) {
+  if (int e = balanced_checks(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales, out, desc)) return e;
+  if (desc->num_seqs == 0) return ok();
+  if (!workspace) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(PKV_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const BalancedLayout lay = balanced_layout(desc);
+  if (workspace_bytes < lay.total)
+    return fail(PKV_ERR_INVALID_ARG, "workspace of %lld bytes is smaller than the %lld needed",
+                static_cast<long long>(workspace_bytes), static_cast<long long>(lay.total));
+  if (lay.slots > 0x7FFFFFFF / 16) return fail(PKV_ERR_INVALID_ARG, "too many partial slots");
+  return balanced_run(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales,
+                      static_cast<char*>(workspace), lay, out, desc, stream, "paged_decode_attention_balanced launch");
+}
+
+int paged_decode_attention_balanced_static(const void* q, const void* k_cache, const void* v_cache,
+                                           const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                           const float* kv_scales, void* out, const pkv_desc* desc, void* stream) {
+  if (int e = balanced_checks(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales, out, desc)) return e;
+  if (desc->num_seqs == 0) return ok();
+  const BalancedLayout lay = balanced_layout(desc);
+  if (lay.total > kStaticScratchBytes)
+    return fail(PKV_ERR_INVALID_ARG,
+                "paged_decode_attention_balanced_static needs %lld bytes of scratch; the static buffer holds %lld "
+                "(use paged_decode_attention_balanced with a workspace)",
+                static_cast<long long>(lay.total), static_cast<long long>(kStaticScratchBytes));
+  char* ws = nullptr;
+  if (int e = static_scratch(&ws)) return e;
+  return balanced_run(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales, ws, lay, out, desc, stream,
+                      "paged_decode_attention_balanced_static launch");
 }
 
 int64_t paged_prefill_workspace_bytes(const pkv_desc* desc, int32_t num_query_tokens, int32_t partition_size) {
