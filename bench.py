@@ -4,7 +4,10 @@
 
 One step = one decode-attention step of one layer for the whole batch: the
 new-token slot write (for workloads that have one), the split-context
-partial kernel and the LSE merge kernel, all through the C ABI.  Each step
+kernel and the LSE merge kernel, all through the C ABI.  The headline runs
+the balanced schedule (paged_decode_attention_balanced_partial and _reduce:
+equal tile shares per compute unit, split points chosen by load, no
+partition size); --path picks another.  Each step
 uses the next of several layer pools in turn (distinct HBM buffers, more
 bytes than the 256 MB Infinity Cache holds), as consecutive layers of a real
 decode step do, so every step reads its K/V from HBM.
@@ -12,11 +15,11 @@ decode step do, so every step reads its K/V from HBM.
 Prints ONE JSON line.  ``value`` is the headline workload's K/V-read
 throughput: unique K/V bytes per step (each physical (block, kv head) tile
 counted once, by the tokens read from it) over the wall time per step.
-``roofline`` rates the partial kernel alone: the same bytes over its average
+``roofline`` rates the split kernel alone: the same bytes over its average
 duration, measured inside the timed region with HIP events recorded on the
 stream the kernel runs on (events created with hipEventDisableSystemFence,
 which costs about 1 us per step instead of about 5).  ``cpu_baseline`` is the
-float64 oracle on the host, one thread, on the same batch.  A second workload
+float64 oracle on all the host's cores (one worker process per core), on the same batch.  A second workload
 (the B=32 Qwen2.5-1.5B-shaped layer with its new-token write) is timed in the
 same run and reported as ``b32``.  The other rows of the path (FP8 E4M3
 decode, the sliding window, the multi-token step, the E4M3 quantiser and
@@ -103,18 +106,25 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def counters_traffic(workload: str, digest: str):
-    """HBM bytes per partial-kernel launch from the committed rocprofv3 counter
-    summary, if it was taken from the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"paged_decode_{workload}_hbm_counters.txt")
-    if not os.path.exists(path):
+# Kernel whose counters the committed HBM summary must hold, per path.
+PATH_KERNEL = {"balanced": "paged_decode_cu_stream", "pair": "paged_decode_persistent",
+               "fused": "paged_decode_persistent", "step": "paged_decode_persistent",
+               "single": "paged_decode_persistent"}
+
+
+def counters_traffic(workload: str, digest: str, path: str = "balanced"):
+    """HBM bytes per launch of the path's split kernel from the committed
+    rocprofv3 counter summary, if it was taken from the current kernel
+    sources and for that kernel; else None."""
+    fname = os.path.join(ROOT, "profiles", f"paged_decode_{workload}_hbm_counters.txt")
+    if not os.path.exists(fname):
         return None
     vals = {}
-    for line in open(path):
+    for line in open(fname):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_digest") != digest:
+    if vals.get("kernel_source_digest") != digest or PATH_KERNEL.get(path, "?") not in vals.get("kernel", ""):
         return None
     try:
         return int(float(vals["hbm_bytes_per_dispatch"]))
@@ -174,10 +184,12 @@ class Runner:
                 ev.record(e0 + 1, stream)
             return
         if self.path == "balanced":
-            abi.paged_decode_attention_balanced(self.q, k, v, self.tables, self.lens, self.w.scale, sc,
-                                                self.bws, out=self.out, window=self.spec.window)
+            abi.paged_decode_attention_balanced_partial(self.q, k, v, self.tables, self.lens, self.w.scale, sc,
+                                                        self.bws, self.out, window=self.spec.window)
             if ev is not None:
                 ev.record(e0 + 1, stream)
+            abi.paged_decode_attention_balanced_reduce(self.q, k, self.tables, self.bws, self.out,
+                                                       window=self.spec.window)
         elif self.path == "fused":
             abi.paged_decode_attention_split(self.q, k, v, self.tables, self.lens, self.w.scale, sc,
                                              self.P, self.ws, out=self.out, window=self.spec.window)
@@ -474,7 +486,8 @@ def measure_rows(args, only=None) -> dict:
         torch.cuda.empty_cache()
 
     # FP8 E4M3 decode (per-(block, kv head) scales) and the sliding window:
-    # balanced schedule, kernel time = stream kernel + merge (both in the events).
+    # balanced schedule, kernel time = the tile-stream kernel (the events
+    # bracket it; the merge runs after them, and us_per_step holds both).
     # Each on its fastest path (measured: FP8 balanced 94 us, single pass 96,
     # pair P = 2048 97; sliding window single pass 88 us, balanced 94, pair
     # 106-112).  The window's items are equal (1024 positions each), so one
@@ -671,9 +684,10 @@ def main():
                          ") and print {\"rows\": ...}; no headline line")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other rows of the path (FP8, window, multi-token, quantise, append, copy, write)")
-    ap.add_argument("--path", choices=["pair", "fused", "balanced", "step", "single"], default="pair",
-                    help="partial + reduce kernels, the one-launch split with in-kernel merge, or "
-                         "equal tile shares per wave + merge")
+    ap.add_argument("--path", choices=["pair", "fused", "balanced", "step", "single"], default="balanced",
+                    help="balanced: equal tile shares per compute unit + merge (default); pair: fixed "
+                         "partitions + reduce; fused: the one-launch split with in-kernel merge; step: fused "
+                         "with the new-token write; single: one pass")
     ap.add_argument("--secondary-path", choices=["pair", "fused", "balanced", "step"], default="step",
                     help="path for the B=32 line (its fastest: the fused step, write and attention in one launch)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -722,7 +736,8 @@ def main():
         t2, p2 = r2.run(args.steps, args.warmup)
         k2 = sum(p2) / len(p2)
         b32 = {"workload": f"{SECONDARY}: {DESCRIPTIONS[SECONDARY]}", "path": args.secondary_path,
-               "partition_size": r2.P, "us_per_step": round(t2 * 1e6, 2),
+               "partition_size": None if args.secondary_path == "balanced" else r2.P,
+               "us_per_step": round(t2 * 1e6, 2),
                "dominant_kernel_us": round(k2 * 1e3, 2),
                "kv_GBps": round(r2.unique_bytes / t2 / 1e9, 1),
                "seqs_layers_per_s": round(r2.spec.num_seqs / t2, 1),
@@ -733,7 +748,7 @@ def main():
                             "bytes_are": "unique K/V bytes read per step (the 32 new tokens' writes excluded)",
                             "kernel": {"pair": "paged_decode_persistent, split partial mode",
                                        "fused": "paged_decode_persistent, split mode with in-kernel merge",
-                                       "balanced": "paged_decode_stream + stream_merge_kernel",
+                                       "balanced": "paged_decode_cu_stream (per-compute-unit tile shares)",
                                        "step": "paged_decode_persistent, split mode with the new-token write "
                                                "and in-kernel merge"}[args.secondary_path]}}
         del r2
@@ -764,7 +779,8 @@ def main():
         "config": {
             "workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",
             "num_seqs": s.num_seqs, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
-            "head_dim": s.head_dim, "block_size": 16, "partition_size": r.P,
+            "head_dim": s.head_dim, "block_size": 16,
+            "partition_size": None if args.path == "balanced" else r.P,
             "layer_pools": args.layers, "mean_context": round(float(r.w.context_lens.mean()), 1),
             "kv_bytes_unique": r.unique_bytes, "kv_bytes_logical": r.logical_bytes,
         },
@@ -777,10 +793,10 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": counters_traffic(args.workload, digest),
+            "traffic": counters_traffic(args.workload, digest, args.path),
             "kernel": {"pair": "paged_decode_persistent, split partial mode",
                        "fused": "paged_decode_persistent, split mode with in-kernel merge",
-                       "balanced": "paged_decode_stream + stream_merge_kernel (both inside the events)",
+                       "balanced": "paged_decode_cu_stream (per-compute-unit tile shares)",
                        "step": "paged_decode_persistent, split mode with the new-token write and in-kernel merge",
                        "single": "paged_decode_persistent, single-pass mode"}[args.path],
         },

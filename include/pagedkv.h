@@ -319,15 +319,17 @@ int paged_decode_step(const void* q, const void* k_new, const void* v_new, void*
 
 /*
  * paged_decode_attention_balanced - the same attention output, with the
- * split-context work cut so that every wave of the GPU gets an equal share
- * of 16-token tiles whatever the mix of context lengths (flash-decoding's
- * split and log-sum-exp merge as above, with split points chosen by load
- * instead of at fixed partition_size boundaries).  The tiles of all
- * (sequence, kv head) pairs form one stream, sequence-major, and each wave
- * takes one contiguous stretch of it; where a stretch ends inside a
- * (sequence, kv head), both pieces become partials merged by log-sum-exp in
- * a second kernel on the same stream.  Arguments as paged_decode_attention,
- * plus:
+ * split-context work cut by load instead of at fixed partition_size
+ * boundaries (flash-decoding's split and log-sum-exp merge as above, split
+ * points chosen so that the work is even whatever the mix of context
+ * lengths).  The tiles of all (sequence, kv head) pairs form one stream,
+ * sequence-major.  For f32 / f16 / bf16 caches every compute unit takes an
+ * equal contiguous stretch of it, and the unit's waves share their stretch
+ * at run time; for E4M3 caches every wave of the resident grid takes an
+ * equal stretch.  A (sequence, kv head) cut by a stretch's ends (or, in the
+ * first form, longer than 48 tiles) is finished as partials merged by
+ * log-sum-exp in a second kernel on the same stream.  Arguments as
+ * paged_decode_attention, plus:
  *
  *   workspace        device memory of workspace_bytes >=
  *                    paged_decode_balanced_workspace_bytes(desc) bytes,
@@ -336,8 +338,10 @@ int paged_decode_step(const void* q, const void* k_new, const void* v_new, void*
  *                    the same time must not share a workspace.
  * Requires num_seqs <= 2048 (else PKV_ERR_UNSUPPORTED) and
  * num_seqs * num_kv_heads * max_blocks_per_seq < 2^31.  The summation order
- * depends on the batch's total length and the GPU's compute-unit count, so
- * results agree with the other entry points to rounding, not bitwise.
+ * depends on the batch, the GPU's compute-unit count and (for f32 / f16 /
+ * bf16 caches) on which wave takes which tiles at run time, so results agree
+ * with the other entry points, and two calls of this one with each other,
+ * to fp32 rounding, not bitwise.
  */
 int paged_decode_attention_balanced(const void* q, const void* k_cache, const void* v_cache,
                                     const int32_t* block_tables, const int32_t* context_lens,
@@ -345,8 +349,30 @@ int paged_decode_attention_balanced(const void* q, const void* k_cache, const vo
                                     int64_t workspace_bytes, void* out, const pkv_desc* desc,
                                     void* stream);
 
+/*
+ * paged_decode_attention_balanced_partial / _reduce - the two launches of
+ * paged_decode_attention_balanced, for callers that time or schedule them
+ * apart ("LLM Serving Kernels", section "Evidence standard": the dominant
+ * kernel is measured on its own).  _partial takes the same arguments and
+ * streams the tiles: it writes the out rows of the (sequence, kv head) pairs
+ * finished whole and leaves the partials and per-sequence tile offsets in the
+ * workspace.  _reduce, enqueued after it on the same stream with the same
+ * desc and workspace, merges the partials into the remaining out rows (and
+ * writes zeros for empty contexts).  Together they equal
+ * paged_decode_attention_balanced; the workspace must not be reused in
+ * between.  Errors as paged_decode_attention_balanced.
+ */
+int paged_decode_attention_balanced_partial(const void* q, const void* k_cache, const void* v_cache,
+                                            const int32_t* block_tables, const int32_t* context_lens,
+                                            float scale, const float* kv_scales, void* workspace,
+                                            int64_t workspace_bytes, void* out, const pkv_desc* desc,
+                                            void* stream);
+int paged_decode_attention_balanced_reduce(void* workspace, int64_t workspace_bytes, void* out,
+                                           const pkv_desc* desc, void* stream);
+
 /* Workspace bytes paged_decode_attention_balanced needs on the current
- * device (it grows with the number of waves the device holds), or -1.  */
+ * device (it grows with the device's compute units, or for E4M3 caches with
+ * the number of waves it holds), or -1.  */
 int64_t paged_decode_balanced_workspace_bytes(const pkv_desc* desc);
 
 /*
@@ -356,8 +382,9 @@ int64_t paged_decode_balanced_workspace_bytes(const pkv_desc* desc);
  * forbid allocation.  It allocates nothing and calls no allocating routine;
  * its partials live in a 32 MiB device array inside the library, one copy
  * per GPU, held until the process ends (looked up on the first call on each
- * device, which must be the current device).  Same arguments, kernels and
- * result as paged_decode_attention_balanced.  Problems needing more than
+ * device, which must be the current device).  Same arguments and kernels
+ * as paged_decode_attention_balanced, and its result to fp32 rounding (the
+ * summation order is settled at run time).  Problems needing more than
  * 32 MiB of workspace (paged_decode_balanced_workspace_bytes) return
  * PKV_ERR_INVALID_ARG.  The array keeps the last call's contents and needs no
  * clearing (every byte is written before it is read within a call); calls

@@ -62,6 +62,8 @@ def _load():
         "paged_decode_attention_balanced": (ctypes.c_int, [P, P, P, P, P, F, P, P, I64, P, D, P]),
         "paged_decode_balanced_workspace_bytes": (ctypes.c_int64, [D]),
         "paged_decode_attention_balanced_static": (ctypes.c_int, [P, P, P, P, P, F, P, P, D, P]),
+        "paged_decode_attention_balanced_partial": (ctypes.c_int, [P, P, P, P, P, F, P, P, I64, P, D, P]),
+        "paged_decode_attention_balanced_reduce": (ctypes.c_int, [P, I64, P, D, P]),
         "paged_prefill_attention": (ctypes.c_int, [P, P, P, P, P, P, I32, F, P, I32, P, I64, P, D, P]),
         "paged_prefill_workspace_bytes": (ctypes.c_int64, [D, I32, I32]),
         "paged_decode_num_partitions": (ctypes.c_int64, [D, I32]),
@@ -85,6 +87,7 @@ EXPORTED = ("kv_cache_write", "kv_cache_quantize_e4m3", "kv_cache_append_e4m3", 
             "paged_decode_attention_split", "paged_decode_split_workspace_bytes", "paged_decode_step",
             "paged_decode_attention_balanced", "paged_decode_balanced_workspace_bytes",
             "paged_decode_attention_balanced_static",
+            "paged_decode_attention_balanced_partial", "paged_decode_attention_balanced_reduce",
             "paged_prefill_attention", "paged_prefill_workspace_bytes",
             "paged_decode_num_partitions", "paged_decode_workspace_bytes", "pkv_last_error",
             "pkv_version", "pagedkv_last_error", "pagedkv_version", "pkv_read_bandwidth_probe")
@@ -293,6 +296,28 @@ def paged_decode_attention_balanced(q, k_cache, v_cache, block_tables, context_l
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         float(scale), _ptr(kv_scales), _ptr(workspace), workspace.numel(),
         _ptr(out), ctypes.byref(desc), _stream(stream)))
+    return out
+
+
+def paged_decode_attention_balanced_partial(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales,
+                                            workspace, out, stream=None, window=0):
+    """The first launch of paged_decode_attention_balanced (tiles streamed,
+    whole pairs written to ``out``, partials left in ``workspace``)."""
+    desc = _attn_desc(q, k_cache, block_tables, _code(out), window)
+    _check("paged_decode_attention_balanced_partial", _lib.paged_decode_attention_balanced_partial(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        float(scale), _ptr(kv_scales), _ptr(workspace), workspace.numel(),
+        _ptr(out), ctypes.byref(desc), _stream(stream)))
+    return out
+
+
+def paged_decode_attention_balanced_reduce(q, k_cache, block_tables, workspace, out, stream=None, window=0):
+    """The second launch of paged_decode_attention_balanced: merges the
+    partials the first left in ``workspace`` into ``out`` (q, k_cache and
+    block_tables give the shapes and dtypes, as for the first call)."""
+    desc = _attn_desc(q, k_cache, block_tables, _code(out), window)
+    _check("paged_decode_attention_balanced_reduce", _lib.paged_decode_attention_balanced_reduce(
+        _ptr(workspace), workspace.numel(), _ptr(out), ctypes.byref(desc), _stream(stream)))
     return out
 
 

@@ -98,11 +98,15 @@ SplitLayout split_layout(const pkv_desc* d, int64_t s) {
   return l;
 }
 
-// Balanced workspace: [seq_tiles int32 B+1 | pad to 256][tmp_lse f32 G*slots | pad]
-// [tmp_out f32 G*slots*D], slots = B*Hkv + the resident grid's wave count.
+// Balanced workspace: [seq_tiles int32 B+1 | pad to 256][tmp_lse f32 A*G*slots | pad]
+// [tmp_out f32 A*G*slots*D].  f32 / f16 / bf16 caches run the per-compute-unit
+// schedule: slots = B*Hkv + the compute units, A = 2 arrays of partials (the
+// items' first parts and the rest).  E4M3 caches run the per-wave schedule:
+// slots = B*Hkv + the resident grid's wave count, A = 1.
 struct BalancedLayout {
   int64_t slots, lse_off, out_off, total;
   int32_t workers;
+  bool per_cu;
 };
 int check_balanced(const pkv_desc* d) {
   if (d->num_seqs > pkv::kMaxSeqsPersistent)
@@ -114,12 +118,14 @@ int check_balanced(const pkv_desc* d) {
 }
 BalancedLayout balanced_layout(const pkv_desc* d) {
   BalancedLayout l;
-  l.workers = pkv::stream_max_workers(d->kv_dtype, d->head_dim);
+  l.per_cu = d->kv_dtype != PKV_E4M3;
+  l.workers = l.per_cu ? pkv::cu_stream_workers() : pkv::stream_max_workers(d->kv_dtype, d->head_dim);
   const int64_t G = d->num_q_heads / d->num_kv_heads;
+  const int64_t arrays = l.per_cu ? 2 : 1;
   l.slots = static_cast<int64_t>(d->num_seqs) * d->num_kv_heads + l.workers;
   l.lse_off = align256((static_cast<int64_t>(d->num_seqs) + 1) * 4);
-  l.out_off = l.lse_off + align256(G * l.slots * 4);
-  l.total = l.out_off + G * l.slots * d->head_dim * 4;
+  l.out_off = l.lse_off + align256(arrays * G * l.slots * 4);
+  l.total = l.out_off + arrays * G * l.slots * d->head_dim * 4;
   return l;
 }
 
@@ -437,10 +443,11 @@ static int balanced_checks(const void* q, const void* k_cache, const void* v_cac
 }
 
 // The balanced schedule's two launches on a workspace already checked
-// against lay.
-static int balanced_run(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                        const int32_t* context_lens, float scale, const float* kv_scales, char* ws,
-                        const BalancedLayout& lay, void* out, const pkv_desc* desc, void* stream, const char* what) {
+// against lay: the tile stream, then the merge of the partials.
+static int balanced_main(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, float scale, const float* kv_scales, char* ws,
+                         const BalancedLayout& lay, void* out, const pkv_desc* desc, void* stream,
+                         const char* what) {
   pkv::DecodeParams p = decode_params(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales, desc);
   p.out = out;
   p.seq_tiles = reinterpret_cast<int32_t*>(ws);
@@ -449,23 +456,50 @@ static int balanced_run(const void* q, const void* k_cache, const void* v_cache,
   p.num_workers = lay.workers;
   p.num_slots = static_cast<int32_t>(lay.slots);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (int e = hip_status(pkv::launch_stream(p, desc->kv_dtype, desc->head_dim, st), what)) return e;
+  return hip_status(lay.per_cu ? pkv::launch_cu_stream(p, desc->kv_dtype, desc->head_dim, st)
+                               : pkv::launch_stream(p, desc->kv_dtype, desc->head_dim, st),
+                    what);
+}
+
+static int balanced_merge(char* ws, const BalancedLayout& lay, void* out, const pkv_desc* desc, void* stream,
+                          const char* what) {
   pkv::ReduceParams r{};
-  r.tmp_out = p.tmp_out;
-  r.tmp_lse = p.tmp_lse;
-  r.context_lens = context_lens;
+  r.tmp_out = reinterpret_cast<float*>(ws + lay.out_off);
+  r.tmp_lse = reinterpret_cast<float*>(ws + lay.lse_off);
   r.out = out;
   r.num_seqs = desc->num_seqs;
   r.num_q_heads = desc->num_q_heads;
   r.head_dim = desc->head_dim;
   r.mbps = desc->max_blocks_per_seq;
   r.out_dtype = desc->out_dtype;
-  r.seq_tiles = p.seq_tiles;
+  r.seq_tiles = reinterpret_cast<int32_t*>(ws);
   r.num_kv_heads = desc->num_kv_heads;
-  r.num_workers = p.num_workers;
-  r.num_slots = p.num_slots;
-  r.window = p.window;
-  return hip_status(pkv::launch_stream_merge(r, st), what);
+  r.num_workers = lay.workers;
+  r.num_slots = static_cast<int32_t>(lay.slots);
+  r.window = desc->sliding_window;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(lay.per_cu ? pkv::launch_cu_merge(r, st) : pkv::launch_stream_merge(r, st), what);
+}
+
+static int balanced_run(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                        const int32_t* context_lens, float scale, const float* kv_scales, char* ws,
+                        const BalancedLayout& lay, void* out, const pkv_desc* desc, void* stream, const char* what) {
+  if (int e = balanced_main(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales, ws, lay, out, desc,
+                            stream, what))
+    return e;
+  return balanced_merge(ws, lay, out, desc, stream, what);
+}
+
+// Checks a caller workspace for the balanced schedule.
+static int balanced_workspace_check(const void* workspace, int64_t workspace_bytes, const BalancedLayout& lay) {
+  if (!workspace) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(PKV_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (workspace_bytes < lay.total)
+    return fail(PKV_ERR_INVALID_ARG, "workspace of %lld bytes is smaller than the %lld needed",
+                static_cast<long long>(workspace_bytes), static_cast<long long>(lay.total));
+  if (lay.slots > 0x7FFFFFFF / 16) return fail(PKV_ERR_INVALID_ARG, "too many partial slots");
+  return PKV_OK;
 }
 
 int paged_decode_attention_balanced(const void* q, const void* k_cache, const void* v_cache,
@@ -474,16 +508,36 @@ int paged_decode_attention_balanced(const void* q, const void* k_cache, const vo
                                     void* out, const pkv_desc* desc, void* stream) {
   if (int e = balanced_checks(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales, out, desc)) return e;
   if (desc->num_seqs == 0) return ok();
-  if (!workspace) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
-  if (reinterpret_cast<uintptr_t>(workspace) % 256)
-    return fail(PKV_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
   const BalancedLayout lay = balanced_layout(desc);
-  if (workspace_bytes < lay.total)
-    return fail(PKV_ERR_INVALID_ARG, "workspace of %lld bytes is smaller than the %lld needed",
-                static_cast<long long>(workspace_bytes), static_cast<long long>(lay.total));
-  if (lay.slots > 0x7FFFFFFF / 16) return fail(PKV_ERR_INVALID_ARG, "too many partial slots");
+  if (int e = balanced_workspace_check(workspace, workspace_bytes, lay)) return e;
   return balanced_run(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales,
                       static_cast<char*>(workspace), lay, out, desc, stream, "paged_decode_attention_balanced launch");
+}
+
+int paged_decode_attention_balanced_partial(const void* q, const void* k_cache, const void* v_cache,
+                                            const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                            const float* kv_scales, void* workspace, int64_t workspace_bytes,
+                                            void* out, const pkv_desc* desc, void* stream) {
+  if (int e = balanced_checks(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales, out, desc)) return e;
+  if (desc->num_seqs == 0) return ok();
+  const BalancedLayout lay = balanced_layout(desc);
+  if (int e = balanced_workspace_check(workspace, workspace_bytes, lay)) return e;
+  return balanced_main(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scales,
+                       static_cast<char*>(workspace), lay, out, desc, stream,
+                       "paged_decode_attention_balanced_partial launch");
+}
+
+int paged_decode_attention_balanced_reduce(void* workspace, int64_t workspace_bytes, void* out, const pkv_desc* desc,
+                                           void* stream) {
+  if (int e = check_desc(desc, true)) return e;
+  if (int e = check_balanced(desc)) return e;
+  if (desc->num_seqs == 0) return ok();
+  if (!out) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  const BalancedLayout lay = balanced_layout(desc);
+  if (lay.workers <= 0) return fail(PKV_ERR_UNSUPPORTED, "kv_dtype %d", desc->kv_dtype);
+  if (int e = balanced_workspace_check(workspace, workspace_bytes, lay)) return e;
+  return balanced_merge(static_cast<char*>(workspace), lay, out, desc, stream,
+                        "paged_decode_attention_balanced_reduce launch");
 }
 
 int paged_decode_attention_balanced_static(const void* q, const void* k_cache, const void* v_cache,

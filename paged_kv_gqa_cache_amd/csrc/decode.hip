@@ -267,9 +267,11 @@ __device__ __forceinline__ void store4(void* base, size_t idx, int out_dtype, f3
 // trip.  Loads are bounded buffer loads (past row n they read 0 and get
 // weight 0), so none is conditional.  The order of summation is fixed:
 // s = 0, 1, ...  Returns this lane's D/64 output dims (lane * D/64 + k).
+// Adds n rows to a running merge (max M in log2 units, weight sum wsum,
+// unnormalised sum acc).
 template <int D, bool COH>
-__device__ __forceinline__ void merge_partitions(const float* lse, const float* o_row0, int n, int lane,
-                                                 float (&acc)[D / 64]) {
+__device__ __forceinline__ void merge_rows(const float* lse, const float* o_row0, int n, int lane, float& M,
+                                           float& wsum, float (&acc)[D / 64]) {
   // Every rounding step is spelled out (explicit FMAs, no contraction), so
   // the in-kernel merge and the reduce kernel give the same bits.
 #pragma clang fp contract(off)
@@ -281,10 +283,6 @@ __device__ __forceinline__ void merge_partitions(const float* lse, const float* 
   constexpr int aux = COH ? kDeviceScope : 0;
   const auto lse_r = make_tile_rsrc(lse, n * 4);
   const auto o_r = make_tile_rsrc(o_row0, n * D * 4);
-#pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-  float M = -INFINITY;
-  float wsum = 0.f;
   for (int c = 0; c < n; c += BATCH) {
     float l[BATCH], v[BATCH][PER];
 #pragma unroll
@@ -308,6 +306,73 @@ __device__ __forceinline__ void merge_partitions(const float* lse, const float* 
     for (int k = 0; k < PER; ++k) acc[k] *= alpha;
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
+      const float w = fast_exp2(l[u] - M);
+      wsum += w;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] = __builtin_fmaf(w, v[u][k], acc[k]);
+    }
+  }
+}
+
+template <int D, bool COH>
+__device__ __forceinline__ void merge_partitions(const float* lse, const float* o_row0, int n, int lane,
+                                                 float (&acc)[D / 64]) {
+  constexpr int PER = D / 64;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  float M = -INFINITY;
+  float wsum = 0.f;
+  merge_rows<D, COH>(lse, o_row0, n, lane, M, wsum, acc);
+  const float inv = 1.f / wsum;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] *= inv;
+}
+
+// As merge_partitions over the rows of two arrays, n1 rows at (lse1, o1)
+// and n2 at (lse2, o2); each batch loads eight rows of both arrays in one
+// round trip.
+template <int D>
+__device__ __forceinline__ void merge_partitions2(const float* lse1, const float* o1, int n1, const float* lse2,
+                                                  const float* o2, int n2, int lane, float (&acc)[D / 64]) {
+#pragma clang fp contract(off)
+  constexpr int PER = D / 64;
+  constexpr int BATCH = 8;
+  const auto lse1_r = make_tile_rsrc(lse1, n1 * 4);
+  const auto o1_r = make_tile_rsrc(o1, n1 * D * 4);
+  const auto lse2_r = make_tile_rsrc(lse2, n2 * 4);
+  const auto o2_r = make_tile_rsrc(o2, n2 * D * 4);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  float M = -INFINITY;
+  float wsum = 0.f;
+  const int n = max(n1, n2);
+  for (int c = 0; c < n; c += BATCH) {
+    float l[2 * BATCH], v[2 * BATCH][PER];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      l[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lse1_r, (c + u) * 4, 0, 0));
+      l[BATCH + u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lse2_r, (c + u) * 4, 0, 0));
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const uint32_t off = ((c + u) * D + lane * PER + k) * 4;
+        v[u][k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(o1_r, off, 0, 0));
+        v[BATCH + u][k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(o2_r, off, 0, 0));
+      }
+    }
+    float mc = M;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      l[u] = (c + u < n1) ? l[u] * kLog2e : -INFINITY;
+      l[BATCH + u] = (c + u < n2) ? l[BATCH + u] * kLog2e : -INFINITY;
+      mc = fmaxf(mc, fmaxf(l[u], l[BATCH + u]));
+    }
+    const float alpha = fast_exp2(M - mc);
+    M = mc;
+    wsum *= alpha;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] *= alpha;
+#pragma unroll
+    for (int u = 0; u < 2 * BATCH; ++u) {
       const float w = fast_exp2(l[u] - M);
       wsum += w;
 #pragma unroll
@@ -1280,8 +1345,9 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const ReduceParams p
 }
 
 // ------------------------------------------------------ balanced schedule
-// Every wave of a resident grid is a worker with an equal share of the
-// batch's 16-token tiles, whatever the mix of context lengths.  The tiles
+// Per-wave form (E4M3 caches; the others take the per-compute-unit form
+// below).  Every wave of a resident grid is a worker with an equal share of
+// the batch's 16-token tiles, whatever the mix of context lengths.  The tiles
 // of all (sequence, kv head) items form one stream -- sequence-major, then
 // kv head, then block -- and worker w of R takes tiles [T*w/R, T*(w+1)/R).
 // A share may begin or end inside an item: each piece of an item that a
@@ -1462,6 +1528,591 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const ReduceParams p)
   store_row_part<D>(p.out, pair, lane, p.out_dtype, acc);
 }
 
+// ------------------------------------------------- CU-balanced schedule
+// One workgroup per compute unit, and every unit gets an equal, tile-exact
+// share of the batch's 16-token tiles (the sequence-major stream of the
+// per-wave schedule above, with shares in the place of its workers): the
+// time of a memory-bound step is set by the unit that streams the most.
+// Inside a unit the waves take their tiles at run time.  Waves of one unit
+// do not stream at one rate (measured with equal fixed shares: the wave
+// placed first on a SIMD finished a third earlier than the second), so a
+// fixed split leaves a unit partly idle at its end.
+//
+// Parts and units.  A piece is the part of one (sequence, kv head) item
+// that falls in the share.  Its tiles among the item's first kCuCachedTiles
+// form the piece's first part, loaded with the ordinary cache policy
+// (prompts shared between sequences sit at the start, and the caches keep
+// them for the other sequences); the rest form its second part, streamed
+// (non-temporal).  Each part is cut into units of up to RD consecutive
+// tiles.  Units are numbered over the first parts of all the share's pieces,
+// then over the second parts, and a wave takes the next unit with one LDS
+// atomic add, finding it by walking a cursor of its own forward (the
+// numbers a wave takes only grow).  A unit has one item, so one query
+// operand and one softmax state; and a wave meets all first-part units
+// before any second-part unit, so each phase runs in a loop of its own with
+// a single load policy.
+//
+// A wave keeps a running state for the part it is on.  When its next unit
+// belongs to another part it disposes of the state: a state covering the
+// whole part is written out at once; any other is merged into the part's
+// LDS accumulator (a slot found or taken under an allocation lock, merged
+// under the slot's own lock), and the wave whose merge completes the part's
+// tile count writes the result and frees the slot.  A result is the output
+// when the part is the whole item, else a partial (normalised output and
+// natural-log LSE) in slot item + share of the phase's array, merged across
+// parts and shares by cu_merge_kernel.  No lock is held while waiting for
+// anything else, and a slot is never short: each slot in use belongs to a
+// part that still has tiles in some wave (in its state or in one of the
+// three units it has taken), a wave covers at most four parts, and there
+// are 4 x NW slots.  So no wave ever waits for another wave's tiles.
+//
+// Which wave takes which unit varies from call to call, and so does the
+// order in which a part's tiles are summed: two calls may differ in the
+// last bits of fp32.
+constexpr int kSlotFree = -1;
+constexpr int kSpinLimit = 1 << 22;
+constexpr int kCuCachedTiles = 48;
+
+template <int NT>
+struct CuAcc {
+  f32x4 o[NT][64];   // lane layout of WaveState::o
+  float m[16];       // per head column: reference max (log2 units)
+  float l[16];       // per head column: sum of exp2(x - m)
+};
+
+template <int NT, int NS>
+struct CuShared {
+  CuAcc<NT> acc[NS];
+  int tag[NS];      // ordinal of the part the slot holds, or kSlotFree
+  int tiles[NS];    // tiles merged into the slot so far
+  int lock[NS];     // guards the slot's accumulator and tile count
+  int alloc_lock;   // guards finding or taking a slot for a part
+  int next_unit;    // first unit no wave has taken
+};
+
+// One tile's step of the online softmax for the G heads of a KV head (one
+// wave): logits, lazy max, P, PV.  vexp as in attend_packs (E4M3 only).
+template <int KVT, int D>
+__device__ __forceinline__ void cu_tile(WaveState<D / 16>& st, int& vexp, const u32x4 (&kt)[TileOps<KVT, D>::NLOAD],
+                                        u32x4 (&vt)[TileOps<KVT, D>::NLOAD], float ksc, float vsc,
+                                        const u32x4 (&qop)[TileOps<KVT, D>::NQ], float qk_scale_log2, int tok0,
+                                        int L, int lo, int g) {
+  typedef TileOps<KVT, D> T;
+  constexpr int NT = T::NT;
+  float f = qk_scale_log2;
+  float pscale = 1.f;
+  if constexpr (KVT == KV_E4M3) {
+    f *= ksc;
+    const uint32_t vbits = __builtin_amdgcn_readfirstlane(__float_as_uint(vsc));
+    const int e_blk = static_cast<int>((vbits >> 23) & 0xFFu) - 126;
+    if (e_blk > vexp) {
+      const float shrink = __builtin_amdgcn_ldexpf(1.f, vexp - e_blk);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) st.o[n] *= shrink;
+      vexp = e_blk;
+    }
+    pscale = __builtin_amdgcn_ldexpf(__uint_as_float(vbits), 7 - vexp);
+  }
+  const bool tail = tok0 + kBlockSize > L;
+  if (tail) T::mask_v(vt, L - tok0 - 4 * g);
+  const f32x4 s = T::qk(kt, qop);
+  float x[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = s[j] * f;
+  if (tail) {
+    const int nv = L - tok0 - 4 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = (j < nv) ? x[j] : -INFINITY;
+  }
+  if (tok0 < lo) {
+    const int nlo = lo - tok0 - 4 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = (j < nlo) ? -INFINITY : x[j];
+  }
+  const float bm = max_over_groups(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  if (__any(bm > st.m + kSlack)) {
+    const float m_new = fmaxf(st.m, bm);
+    const float alpha = fast_exp2(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) st.o[n] *= alpha;
+  }
+  float pr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(x[j] - st.m);
+  st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+  T::pv(st.o, vt, pr, pscale);
+}
+
+// Writes a finished part: out (normalised) for a whole item, else the
+// partial pair (normalised output, natural-log LSE) in slot item + share of
+// the phase's array (0: first parts, 1: second parts).
+// Column r of lane (g, r) is query head h*G + r; acc is O^T d-tiles.
+template <int D>
+__device__ __forceinline__ void cu_emit(const DecodeParams& p, int b, int h, int item, int share, int phase,
+                                        bool whole, float M, float Lsum, const f32x4 (&acc)[D / 16], int g, int r) {
+  constexpr int NT = D / 16;
+  const int G = p.group;
+  if (r >= G) return;
+  const float inv = 1.f / Lsum;
+  if (whole) {
+    const size_t row = (static_cast<size_t>(b) * p.num_q_heads + h * G + r) * D;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) store4(p.out, row + 16 * n + 4 * g, p.out_dtype, acc[n] * inv);
+  } else {
+    const size_t slot = static_cast<size_t>(phase * G + r) * p.num_slots + item + share;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(p.tmp_out + slot * D + 16 * n + 4 * g) = acc[n] * inv;
+    if (g == 0) p.tmp_lse[slot] = (M + fast_log2(Lsum)) * kLn2;
+  }
+}
+
+template <int KVT, int D, int NW, int RD>
+__global__ __launch_bounds__(NW * 64) void paged_decode_cu_stream(const DecodeParams p) {
+  typedef TileOps<KVT, D> T;
+  constexpr int NT = T::NT;
+  constexpr int NL = T::NLOAD;
+  constexpr int NQ = T::NQ;
+  constexpr int E = ElemBytes<KVT>::value;
+  constexpr int TILE = kBlockSize * D * E;
+  constexpr int QB = (KVT == KV_F32) ? 4 : 2;
+  // Accumulator slots: a slot is taken by the first wave that parks a
+  // part and freed by the merge that completes it, so every part holding a
+  // slot still has tiles in some wave (in its state or in one of the three
+  // units it has taken), and a wave covers at most four parts: 4 * NW slots
+  // never run out.
+  constexpr int NS = 4 * NW;
+  static_assert(sizeof(CuShared<NT, NS>) + sizeof(int) * (2 * kMaxSeqsPersistent + 1 + NW) > 80 * 1024,
+                "the LDS must keep a second workgroup off the compute unit");
+  __shared__ CuShared<NT, NS> sh;
+  __shared__ int s_cum[kMaxSeqsPersistent + 1];   // tiles before sequence b
+  __shared__ int s_len[kMaxSeqsPersistent];       // context length of sequence b
+  __shared__ int s_wsum[NW];
+  const int B = p.num_seqs;
+  const int Hkv = p.num_kv_heads;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  const int G = p.group;
+
+  if (threadIdx.x < NS) {
+    sh.tag[threadIdx.x] = kSlotFree;
+    sh.tiles[threadIdx.x] = 0;
+    sh.lock[threadIdx.x] = 0;
+  }
+  if (threadIdx.x == 0) {
+    sh.next_unit = NW;   // units 0 .. NW - 1 are the waves' first, taken without the counter
+    sh.alloc_lock = 0;
+  }
+  // Exclusive prefix sum over sequences of Hkv * (tiles from the window's
+  // first block to the end).
+  int carry = 0;
+  for (int c = 0; c < B; c += NW * 64) {
+    const int i = c + static_cast<int>(threadIdx.x);
+    int tiles = 0;
+    if (i < B) {
+      const int L = max(0, min(p.context_lens[i], p.mbps * kBlockSize));
+      s_len[i] = L;
+      tiles = Hkv * ((L + kBlockSize - 1) / kBlockSize - window_block(L, p.window));
+    }
+    int x = tiles;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wsum[wid] = x;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wid; ++w) before += s_wsum[w];
+    int total = 0;
+    for (int w = 0; w < NW; ++w) total += s_wsum[w];
+    if (i < B) s_cum[i + 1] = before + x;
+    if (i == 0) s_cum[0] = 0;
+    carry += total;
+    __syncthreads();
+  }
+  const int Tt = carry;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= B; i += NW * 64) p.seq_tiles[i] = s_cum[i];
+  // Share of this workgroup: consecutive shares sit on one XCD (workgroup k
+  // runs on XCD k % 8), so neighbouring sequences, the ones likely to share
+  // prompt blocks, go through one L2.  A small batch uses fewer shares, at
+  // least kMinTilesPerWorker tiles each, so no share is empty (the merge
+  // takes every share an item spans).
+  const int nwg = gridDim.x;
+  const int R = stream_workers(Tt, nwg);
+  const int share = (nwg % kXcds == 0)
+                        ? static_cast<int>(blockIdx.x % kXcds) * (nwg / kXcds) + static_cast<int>(blockIdx.x) / kXcds
+                        : static_cast<int>(blockIdx.x);
+  if (share >= R) return;
+  const int t0 = static_cast<int>(static_cast<int64_t>(Tt) * share / R);
+  const int t1 = static_cast<int>(static_cast<int64_t>(Tt) * (share + 1) / R);
+  if (t1 <= t0) return;
+
+  // Parts.  Every piece has a first part, its tiles among the first
+  // kCuCachedTiles of the item (loaded with the ordinary cache policy), and
+  // a second part, the rest (streamed); either may be empty.  Units are
+  // numbered over the first parts of all the share's pieces, then over the
+  // second parts, so a wave's units run through the first phase and then
+  // the second, and each phase has a loop of its own with one load policy
+  // (a branch between policies around the loads would make the compiler
+  // wait for every load in flight).  Parts are numbered the same way (part
+  // ordinal pk: piece index in the first phase, pieces + piece index in the
+  // second), the order in which their units are taken.
+  //
+  // The wave's cursor: the piece (item (b, h), whose nb tiles are stream
+  // tiles s_i .. s_i + nb - 1; the piece is stream tiles [ps, pe)), the
+  // phase, the first unit of the current part (ubase) and its ordinal.
+  struct Cursor {
+    int b, h, nb, s_i, ps, pe, ubase, pk, phase;
+  };
+  auto item_tiles = [&](int b) __attribute__((always_inline)) {
+    const int L = s_len[b];
+    return __builtin_amdgcn_readfirstlane((L + kBlockSize - 1) / kBlockSize - window_block(L, p.window));
+  };
+  auto set_piece = [&](Cursor& c) __attribute__((always_inline)) {
+    c.s_i = __builtin_amdgcn_readfirstlane(s_cum[c.b]) + c.h * c.nb;
+    c.ps = max(c.s_i, t0);
+    c.pe = min(c.s_i + c.nb, t1);
+  };
+  // Stream tiles [qa, qb) of the cursor's part (qb <= qa: empty).
+  auto part_of = [&](const Cursor& c, int& qa, int& qb) __attribute__((always_inline)) {
+    const int cut = c.s_i + kCuCachedTiles;
+    qa = c.phase == 0 ? c.ps : max(c.ps, cut);
+    qb = c.phase == 0 ? min(c.pe, cut) : c.pe;
+  };
+  auto part_units = [&](const Cursor& c) __attribute__((always_inline)) {
+    int qa, qb;
+    part_of(c, qa, qb);
+    return qb > qa ? (qb - qa + RD - 1) / RD : 0;
+  };
+  Cursor first;
+  {
+    // Sequence of tile t0: the last b with s_cum[b] <= t0, by a two-level
+    // 64-way search (each level one LDS read per lane and a ballot; B <=
+    // 4096, and s_cum[0] = 0 <= t0 sets the first bit of each ballot).
+    const int stride = (B + 63) / 64;
+    const int i1 = lane * stride;
+    const uint64_t m1 = __ballot(i1 < B && s_cum[min(i1, B - 1)] <= t0);
+    const int base = (63 - __builtin_clzll(m1)) * stride;
+    const int i2 = base + lane;
+    const uint64_t m2 = __ballot(lane < stride && i2 < B && s_cum[min(i2, B - 1)] <= t0);
+    const int lo_b = __builtin_amdgcn_readfirstlane(base + 63 - __builtin_clzll(m2));
+    first.b = lo_b;
+    first.nb = item_tiles(lo_b);
+    first.h = (t0 - __builtin_amdgcn_readfirstlane(s_cum[lo_b])) / first.nb;
+    set_piece(first);
+    first.ubase = 0;
+    first.pk = 0;
+    first.phase = 0;
+  }
+  Cursor cur = first;
+  __syncthreads();   // slot tags, locks and the unit counter are set
+
+  const char* kcache = static_cast<const char*>(p.k_cache);
+  const char* vcache = static_cast<const char*>(p.v_cache);
+  uint32_t lane_off[NL];
+#pragma unroll
+  for (int m = 0; m < NL; ++m) lane_off[m] = static_cast<uint32_t>(lane) * 16u + m * 1024u;
+  const auto scale_r = make_tile_rsrc(p.kv_scales, KVT == KV_E4M3 ? 2 * p.num_blocks * Hkv * 4 : 0);
+
+  // A unit taken by this wave.
+  struct Claim {
+    int b, h, j0, n;   // item (sequence b, kv head h), first block index, tiles (0: no unit left)
+    int pk, len;       // part ordinal and its tile count
+    int phase;         // 0: first part (cached), 1: second part (streamed)
+    int whole;         // the part is the whole item
+    int id;            // lane k < n: physical block of tile k
+  };
+  // Unit u (u < 0: the next one from the counter).
+  auto claim = [&](Claim& C, int u = -1) __attribute__((always_inline)) {
+    if (u < 0) {
+      if (lane == 0) u = __hip_atomic_fetch_add(&sh.next_unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      u = __builtin_amdgcn_readfirstlane(u);
+    }
+    while (true) {
+      if (cur.ps >= t1) {   // past the share's last piece
+        if (cur.phase == 1) break;
+        const int ub = cur.ubase, pk = cur.pk;
+        cur = first;        // second phase: the pieces again, from the first
+        cur.phase = 1;
+        cur.ubase = ub;
+        cur.pk = pk;
+        continue;
+      }
+      const int units = part_units(cur);
+      if (u < cur.ubase + units) break;
+      cur.ubase += units;
+      ++cur.pk;
+      if (++cur.h == Hkv) {
+        cur.h = 0;
+        ++cur.b;
+      }
+      if (cur.b < B) {
+        if (cur.h == 0) cur.nb = item_tiles(cur.b);
+        set_piece(cur);
+      } else {
+        cur.ps = cur.pe = t1;
+      }
+    }
+    if (cur.ps < t1) {
+      int qa, qb;
+      part_of(cur, qa, qb);
+      const int ts = qa + (u - cur.ubase) * RD;   // the unit's first stream tile
+      C.b = cur.b;
+      C.h = cur.h;
+      C.n = min(RD, qb - ts);
+      C.j0 = window_block(__builtin_amdgcn_readfirstlane(s_len[cur.b]), p.window) + (ts - cur.s_i);
+      C.pk = cur.pk;
+      C.len = qb - qa;
+      C.phase = cur.phase;
+      C.whole = qa == cur.s_i && qb == cur.s_i + cur.nb;
+    } else {
+      C.b = C.h = C.j0 = C.n = 0;
+      C.pk = -1;
+      C.len = C.phase = C.whole = 0;
+    }
+    // Unconditional load (lanes without a tile read the unit's first entry).
+    C.id = p.block_tables[static_cast<size_t>(C.b) * p.mbps + C.j0 + (lane < C.n ? lane : 0)];
+  };
+
+  // Ring of RD tile buffers: buffer k holds tile k of the unit being processed.
+  u32x4 kb[RD][NL], vb[RD][NL];
+  float ks[RD], vs[RD];
+#pragma unroll
+  for (int k = 0; k < RD; ++k) ks[k] = vs[k] = 1.f;
+  auto load_tile = [&](int k, const Claim& C, auto policy) __attribute__((always_inline)) {
+    constexpr int POL = decltype(policy)::value;
+    const bool valid = k < C.n;
+    const int blk = __builtin_amdgcn_readlane(C.id, k);
+    const size_t tile = (static_cast<size_t>(valid ? blk : 0) * Hkv + C.h) * TILE;
+    if constexpr (KVT == KV_E4M3) {
+      const uint32_t so = static_cast<uint32_t>((valid ? blk : 0) * Hkv + C.h) * 4u;
+      ks[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(scale_r, so, 0, 0));
+      vs[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            scale_r, so + static_cast<uint32_t>(p.num_blocks * Hkv) * 4u, 0, 0));
+    }
+    const auto kr = make_tile_rsrc(kcache + tile, valid ? TILE : 0);
+    const auto vr = make_tile_rsrc(vcache + tile, valid ? TILE : 0);
+#pragma unroll
+    for (int m = 0; m < NL; ++m) kb[k][m] = buffer_ld16_policy<POL>(kr, lane_off[m]);
+#pragma unroll
+    for (int m = 0; m < NL; ++m) vb[k][m] = buffer_ld16_policy<POL>(vr, lane_off[m]);
+  };
+  // Query operand of a unit's item: head column r of the group (a zero-size
+  // descriptor when there is no unit: every load still issues).
+  auto load_q = [&](u32x4 (&qop)[NQ], const Claim& C) __attribute__((always_inline)) {
+    const auto qr = make_tile_rsrc(
+        static_cast<const char*>(p.q) + (static_cast<size_t>(C.b) * p.num_q_heads + C.h * G) * D * QB,
+        C.n > 0 ? G * D * QB : 0);
+    T::load_q(qop, qr, static_cast<uint32_t>(r * D * QB), g);
+  };
+
+  // The wave's running state and its part.
+  WaveState<NT> st;
+  int vexp = -126;
+  int cpk = -1, cb = 0, chh = 0, clen = 0, cphase = 0, cwhole = 0, ccount = 0;
+
+  // Dispose of the state of the current part (ccount of its clen tiles).
+  auto finish_state = [&]() __attribute__((always_inline)) {
+    const int item = cb * Hkv + chh;
+    if constexpr (KVT == KV_E4M3) {
+      const float grow = __builtin_amdgcn_ldexpf(1.f, vexp - 7);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) st.o[n] *= grow;
+    }
+    float l_col = sum_over_groups(st.l);
+    if (ccount == clen) {   // the whole part is in this state
+      cu_emit<D>(p, cb, chh, item, share, cphase, cwhole, st.m, l_col, st.o, g, r);
+      return;
+    }
+    // Find the part's slot, or take a free one (the first wave to park the
+    // part), under the allocation lock; then merge under the slot's lock.
+    // Neither lock is held while waiting for anything else.
+    auto spin_lock = [&](int* l) __attribute__((always_inline)) {
+      for (int it = 0; it < kSpinLimit; ++it) {
+        int got = 0;
+        if (lane == 0) {
+          int expected = 0;
+          got = __hip_atomic_compare_exchange_strong(l, &expected, 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        if (__builtin_amdgcn_readfirstlane(got)) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    auto unlock = [&](int* l) __attribute__((always_inline)) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      if (lane == 0) __hip_atomic_store(l, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    int slot = 0;
+    for (int it = 0; it < kSpinLimit; ++it) {   // one pass: a free slot exists (see NS)
+      spin_lock(&sh.alloc_lock);
+      const int t_lane = lane < NS ? sh.tag[lane] : 0;
+      const uint64_t hit = __ballot(lane < NS && t_lane == cpk);
+      const uint64_t free_slots = __ballot(lane < NS && t_lane == kSlotFree);
+      if (hit || free_slots) {
+        slot = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit ? hit : free_slots)));
+        if (!hit && lane == 0) {
+          sh.tag[slot] = cpk;
+          sh.tiles[slot] = 0;
+        }
+        unlock(&sh.alloc_lock);
+        break;
+      }
+      unlock(&sh.alloc_lock);
+      __builtin_amdgcn_s_sleep(1);
+    }
+    CuAcc<NT>& a = sh.acc[slot];
+    spin_lock(&sh.lock[slot]);
+    const int before = __builtin_amdgcn_readfirstlane(sh.tiles[slot]);
+    bool done = false;
+    if (before == 0) {   // the first share of the part to arrive
+#pragma unroll
+      for (int n = 0; n < NT; ++n) a.o[n][lane] = st.o[n];
+      if (g == 0) {
+        a.m[r] = st.m;
+        a.l[r] = l_col;
+      }
+      if (lane == 0) sh.tiles[slot] = ccount;
+    } else {             // merge with what is there
+      const float ms = a.m[r];
+      const float mn = fmaxf(ms, st.m);
+      const float fs = fast_exp2(ms - mn);
+      const float fw = fast_exp2(st.m - mn);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) st.o[n] = a.o[n][lane] * fs + st.o[n] * fw;
+      l_col = a.l[r] * fs + l_col * fw;
+      st.m = mn;
+      const int total = before + ccount;
+      done = total == clen;
+      if (done) {
+        if (lane == 0) sh.tag[slot] = kSlotFree;
+      } else {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) a.o[n][lane] = st.o[n];
+        if (g == 0) {
+          a.m[r] = mn;
+          a.l[r] = l_col;
+        }
+        if (lane == 0) sh.tiles[slot] = total;
+      }
+    }
+    unlock(&sh.lock[slot]);
+    if (done) cu_emit<D>(p, cb, chh, item, share, cphase, cwhole, st.m, l_col, st.o, g, r);
+  };
+
+  constexpr std::integral_constant<int, 0> kCached{};
+  constexpr std::integral_constant<int, kStreamLoad> kStream{};
+  // P: the unit being processed (tiles in the ring, q in qop); N: the next
+  // unit (ids loaded, q loading into qn, tiles loading as P's buffers free
+  // up); Z: taken at the top of each round (ids loading).
+  Claim P, N, Z;
+  u32x4 qop[NQ], qn[NQ];
+  // One round: P's tiles through the state; tile k of N goes into buffer k
+  // as soon as it is free (a zero-size load past N's end), with the given
+  // cache policy.
+  auto round = [&](auto policy) __attribute__((always_inline)) {
+    claim(Z);
+    load_q(qn, N);
+    if (P.pk != cpk) {   // a unit has one part: switch between units only
+      if (cpk >= 0) finish_state();
+      st.reset();
+      vexp = -126;
+      cpk = P.pk;
+      cb = P.b;
+      chh = P.h;
+      clen = P.len;
+      cphase = P.phase;
+      cwhole = P.whole;
+      ccount = 0;
+    }
+    const int L = __builtin_amdgcn_readfirstlane(s_len[P.b]);
+    const int lo = window_lo(L, p.window);
+#pragma unroll
+    for (int k = 0; k < RD; ++k) {
+      if (k < P.n) {
+        cu_tile<KVT, D>(st, vexp, kb[k], vb[k], ks[k], vs[k], qop, p.qk_scale_log2, (P.j0 + k) * kBlockSize, L,
+                        lo, g);
+        ++ccount;
+      }
+      load_tile(k, N, policy);
+    }
+  };
+  auto rotate = [&]() __attribute__((always_inline)) {
+    P = N;
+    N = Z;
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) qop[m] = qn[m];
+  };
+  claim(P, wid);
+  if (P.n == 0) return;
+  load_q(qop, P);
+  claim(N);
+#pragma unroll
+  for (int k = 0; k < RD; ++k) load_tile(k, P, kCached);   // (a second-part first unit is cached too)
+  // First phase: N's tiles cached.
+  while (N.n > 0 && N.phase == 0) {
+    round(kCached);
+    rotate();
+  }
+  // Second phase: N's tiles streamed (or none).
+  while (true) {
+    round(kStream);
+    if (N.n == 0) break;
+    rotate();
+  }
+  finish_state();
+}
+
+// Merges, per (sequence, query head), the parts of items that were not
+// written whole: item i's first parts sit in slots i + w of the first
+// array for the shares w0 .. wa holding its first kCuCachedTiles tiles, its
+// second parts in slots i + w of the second array for the shares wb .. w1
+// holding the rest; an empty context gets zeros.
+template <int D>
+__global__ __launch_bounds__(256) void cu_merge_kernel(const ReduceParams p) {
+  const int lane = threadIdx.x & 63;
+  const int pair = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));  // wave-uniform
+  if (pair >= p.num_seqs * p.num_q_heads) return;
+  const int b = pair / p.num_q_heads;
+  const int qh = pair % p.num_q_heads;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int h = qh / G;
+  const int gg = qh % G;
+  const int s0 = p.seq_tiles[b];
+  const int nb = (p.seq_tiles[b + 1] - s0) / p.num_kv_heads;
+  const int T = p.seq_tiles[p.num_seqs];
+  float acc[D / 64];
+  if (nb == 0) {
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) acc[k] = 0.f;
+    store_row_part<D>(p.out, pair, lane, p.out_dtype, acc);
+    return;
+  }
+  const int R = stream_workers(T, p.num_workers);
+  const int64_t s = s0 + static_cast<int64_t>(h) * nb;
+  const int na = min(nb, kCuCachedTiles);   // tiles of the first parts
+  const int w0 = stream_worker_of(s, T, R);
+  const int wa = stream_worker_of(s + na - 1, T, R);
+  if (na == nb && w0 == wa) return;        // one part, the whole item: written directly
+  const int item = b * p.num_kv_heads + h;
+  const size_t first = (static_cast<size_t>(gg) * p.num_slots + item + w0);
+  int wb = 0, nparts_b = 0;
+  if (nb > na) {
+    wb = stream_worker_of(s + na, T, R);
+    nparts_b = stream_worker_of(s + nb - 1, T, R) - wb + 1;
+  }
+  const size_t second = (static_cast<size_t>(G + gg) * p.num_slots + item + wb);
+  merge_partitions2<D>(p.tmp_lse + first, p.tmp_out + first * D, wa - w0 + 1, p.tmp_lse + second,
+                       p.tmp_out + second * D, nparts_b, lane, acc);
+  store_row_part<D>(p.out, pair, lane, p.out_dtype, acc);
+}
+
 // ----------------------------------------------------------------- reduce
 // One wave per (sequence, query head) merges its non-empty partitions.
 template <int D>
@@ -1585,25 +2236,77 @@ hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, int 
   return hipErrorInvalidValue;
 }
 
+// The per-wave balanced schedule serves E4M3 caches (their tiles carry
+// twice the arithmetic per byte, which two waves per SIMD hide and the
+// per-compute-unit schedule's one wave per SIMD does not).
 int stream_max_workers(int kv_dtype, int head_dim) {
-  int grid = 0;
-  switch (kv_dtype) {
-    case KV_F32: grid = head_dim == 64 ? stream_grid<KV_F32, 64>() : stream_grid<KV_F32, 128>(); break;
-    case KV_F16: grid = head_dim == 64 ? stream_grid<KV_F16, 64>() : stream_grid<KV_F16, 128>(); break;
-    case KV_BF16: grid = head_dim == 64 ? stream_grid<KV_BF16, 64>() : stream_grid<KV_BF16, 128>(); break;
-    case KV_E4M3: grid = head_dim == 64 ? stream_grid<KV_E4M3, 64>() : stream_grid<KV_E4M3, 128>(); break;
-  }
+  if (kv_dtype != KV_E4M3) return 0;
+  const int grid = head_dim == 64 ? stream_grid<KV_E4M3, 64>() : stream_grid<KV_E4M3, 128>();
   return grid * kWaves;
 }
 
 hipError_t launch_stream(const DecodeParams& p, int kv_dtype, int head_dim, hipStream_t stream) {
-  switch (kv_dtype) {
-    case KV_F32: return head_dim == 64 ? launch_stream_t<KV_F32, 64>(p, stream) : launch_stream_t<KV_F32, 128>(p, stream);
-    case KV_F16: return head_dim == 64 ? launch_stream_t<KV_F16, 64>(p, stream) : launch_stream_t<KV_F16, 128>(p, stream);
-    case KV_BF16: return head_dim == 64 ? launch_stream_t<KV_BF16, 64>(p, stream) : launch_stream_t<KV_BF16, 128>(p, stream);
-    case KV_E4M3: return head_dim == 64 ? launch_stream_t<KV_E4M3, 64>(p, stream) : launch_stream_t<KV_E4M3, 128>(p, stream);
+  if (kv_dtype != KV_E4M3) return hipErrorInvalidValue;
+  return head_dim == 64 ? launch_stream_t<KV_E4M3, 64>(p, stream) : launch_stream_t<KV_E4M3, 128>(p, stream);
+}
+
+// CU-balanced schedule: waves per workgroup (one workgroup per compute
+// unit) and tiles per unit.  The accumulator slots take 4 x waves x
+// (16 x D x 4 + 128) bytes of LDS: at D = 128 four waves (one per SIMD,
+// up to 512 registers each) fill 133 KiB, at D = 64 eight waves 135 KiB.
+// A unit's tiles are also the wave's ring (tiles in flight): six at D = 128
+// (16-bit) measured ~1 us faster than four or eight on the ragged B = 128
+// layer; f32 tiles are twice the size.
+template <int KVT, int D>
+constexpr int cu_waves() {
+  return D == 128 ? 4 : 8;
+}
+template <int KVT, int D>
+constexpr int cu_ring() {
+  return KVT == KV_F32 ? (D == 64 ? 2 : 4) : (D == 128 ? 6 : 4);
+}
+
+int cu_stream_workers() {
+  static std::atomic<int> cached[16];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 16) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
-  return hipErrorInvalidValue;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev < 16) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// The grid is one workgroup per compute unit (the kernel's LDS, over half
+// of a unit's 160 KiB, keeps a second one off every unit).
+template <int KVT, int D>
+static hipError_t launch_cu_stream_t(const DecodeParams& p, hipStream_t stream) {
+  constexpr int NW = cu_waves<KVT, D>();
+  if (p.num_workers <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((paged_decode_cu_stream<KVT, D, NW, cu_ring<KVT, D>()>), dim3(static_cast<unsigned>(p.num_workers)),
+                     dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_cu_stream(const DecodeParams& p, int kv_dtype, int head_dim, hipStream_t stream) {
+  switch (kv_dtype) {
+    case KV_F32: return head_dim == 64 ? launch_cu_stream_t<KV_F32, 64>(p, stream) : launch_cu_stream_t<KV_F32, 128>(p, stream);
+    case KV_F16: return head_dim == 64 ? launch_cu_stream_t<KV_F16, 64>(p, stream) : launch_cu_stream_t<KV_F16, 128>(p, stream);
+    case KV_BF16: return head_dim == 64 ? launch_cu_stream_t<KV_BF16, 64>(p, stream) : launch_cu_stream_t<KV_BF16, 128>(p, stream);
+  }
+  return hipErrorInvalidValue;   // E4M3 caches take the per-wave schedule
+}
+
+hipError_t launch_cu_merge(const ReduceParams& p, hipStream_t stream) {
+  const int pairs = p.num_seqs * p.num_q_heads;
+  if (pairs == 0) return hipSuccess;
+  const dim3 grid((pairs + 3) / 4), block(256);
+  if (p.head_dim == 64) hipLaunchKernelGGL(cu_merge_kernel<64>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(cu_merge_kernel<128>, grid, block, 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_stream_merge(const ReduceParams& p, hipStream_t stream) {

@@ -115,6 +115,12 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
 int stream_max_workers(int kv_dtype, int head_dim);
 hipError_t launch_stream(const DecodeParams& p, int kv_dtype, int head_dim, hipStream_t stream);
 hipError_t launch_stream_merge(const ReduceParams& p, hipStream_t stream);
+// CU-balanced schedule: one workgroup per compute unit (cu_stream_workers()
+// of them on the current device), equal tile shares per unit; items split
+// between units are merged by launch_stream_merge.
+int cu_stream_workers();
+hipError_t launch_cu_stream(const DecodeParams& p, int kv_dtype, int head_dim, hipStream_t stream);
+hipError_t launch_cu_merge(const ReduceParams& p, hipStream_t stream);
 // Multi-token step: mode 0 one pass to out, 1 partials; then the merge.
 hipError_t launch_prefill(const DecodeParams& p, int kv_dtype, int head_dim, int mode, hipStream_t stream);
 hipError_t launch_prefill_merge(const ReduceParams& p, hipStream_t stream);

@@ -151,6 +151,30 @@ def test_balanced_rejects_before_touching_the_device():
     assert balanced(desc(num_seqs=0), ptr=None) == OK
 
 
+def test_balanced_partial_and_reduce_reject_before_touching_the_device():
+    lib = abi.lib()
+
+    def partial(d, ws=FAKE, nbytes=1 << 30, ptr=FAKE):
+        return lib.paged_decode_attention_balanced_partial(ptr, ptr, ptr, ptr, ptr, 0.125, None, ws, nbytes, ptr,
+                                                           ctypes.byref(d), None)
+
+    def reduce(d, ws=FAKE, nbytes=1 << 30, out=FAKE):
+        return lib.paged_decode_attention_balanced_reduce(ws, nbytes, out, ctypes.byref(d), None)
+
+    assert partial(desc(num_seqs=2049)) == UNSUPPORTED
+    assert partial(desc(), ptr=None) == INVALID
+    assert partial(desc(), ws=ctypes.c_void_p(0x1010)) == INVALID
+    assert partial(desc(), nbytes=16) == INVALID
+    assert "smaller" in abi.last_error()
+    assert partial(desc(num_seqs=0), ptr=None) == OK
+    assert reduce(desc(num_seqs=2049)) == UNSUPPORTED
+    assert reduce(desc(), out=None) == INVALID
+    assert reduce(desc(), ws=None) == INVALID
+    assert reduce(desc(), ws=ctypes.c_void_p(0x1010)) == INVALID
+    assert reduce(desc(), nbytes=16) == INVALID
+    assert reduce(desc(num_seqs=0), out=None) == OK
+
+
 def test_copy_blocks_validates_before_touching_the_device():
     lib = abi.lib()
     d = desc()

@@ -28,6 +28,9 @@ def test_committed_counters_match_the_kernel_sources():
     traffic = bench.counters_traffic(bench.HEADLINE, bench.source_digest())
     assert traffic is not None, "profiles/ counter summary was taken from other kernel sources"
     assert 250e6 < traffic < 400e6
+    # the summary holds the balanced schedule's kernel, so another path gets none
+    assert bench.counters_traffic(bench.HEADLINE, bench.source_digest(), "pair") is None
+    assert bench.counters_traffic(bench.HEADLINE, "0" * 16) is None
 
 
 def test_every_committed_kernel_profile_names_the_current_sources():

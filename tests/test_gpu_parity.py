@@ -272,8 +272,19 @@ def test_out_in_query_dtype_is_fp32_out_rounded(name, mode):
     o16 = decode(w, pool, mode, out_dtype=odt)
     rounded = o32.to(odt)
     # within one unit in the last place of the 16-bit type
-    ulp = (rounded.float().abs() * (2.0 ** -10 if odt == torch.float16 else 2.0 ** -7)).clamp_min(1e-30)
-    assert torch.all((o16.float() - rounded.float()).abs() <= ulp)
+    # (f16 values below 2^-14 are subnormal: their spacing is 2^-24)
+    ulp = (rounded.float().abs() * (2.0 ** -10 if odt == torch.float16 else 2.0 ** -7)).clamp_min(
+        2.0 ** -24 if odt == torch.float16 else 1e-30)
+    if mode == "balanced":
+        # Two calls of the balanced schedule may sum in different orders
+        # (waves claim tiles at run time): the 16-bit output is its own
+        # call's fp32 result rounded to nearest, so it lies within half an
+        # ulp of that, and the two calls' fp32 results differ by an fp32
+        # summation-order error (absolute: ~1e-7 on these unit-scale
+        # values, also where the output itself is near zero).
+        assert torch.all((o16.float() - o32).abs() <= 0.5 * ulp + 2e-6)
+    else:
+        assert torch.all((o16.float() - rounded.float()).abs() <= ulp)
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen25_1p5b"])
@@ -397,7 +408,31 @@ def test_balanced_with_many_sequences(lengths):
     assert max_err(decode(w, gpu_pool(w), "balanced"), oracle_out(w)) <= TOL
 
 
-def test_balanced_is_deterministic_and_reuses_its_workspace():
+@pytest.mark.parametrize("name", ["tiny", "smollm2_360m", "qwen25_7b_prefix", "qwen25_7b_fp8"])
+def test_balanced_partial_then_reduce_is_the_one_call(name):
+    """The two launches of the balanced schedule called apart (as the
+    benchmark times the first) give the one-call result: within fp32
+    summation-order differences of it, and within the oracle's tolerance."""
+    _announce("balanced partial + reduce", name)
+    from paged_kv_gqa_cache_amd import abi
+    w = workloads.generate(name, **REDUCED.get(name, {}))
+    pool = gpu_pool(w)
+    k, v, sc = pool
+    q, tables, lens = inputs(w)
+    ws = abi.balanced_workspace(q, k, tables)
+    one = abi.paged_decode_attention_balanced(q, k, v, tables, lens, w.scale, sc, ws)
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    abi.paged_decode_attention_balanced_partial(q, k, v, tables, lens, w.scale, sc, ws, out)
+    abi.paged_decode_attention_balanced_reduce(q, k, tables, ws, out)
+    torch.cuda.synchronize()
+    assert float((out - one).abs().max()) <= 1e-5
+    assert max_err(out, oracle_out(w)) <= TOL
+
+
+def test_balanced_runs_agree_and_reuse_their_workspace():
+    """Ten calls on one workspace: each within the oracle's tolerance, and
+    all within fp32 summation-order differences of each other (the waves of
+    a compute unit claim tiles at run time, so the order is not fixed)."""
     _announce("balanced reuse")
     from paged_kv_gqa_cache_amd import abi
     w = workloads.generate("qwen25_7b_prefix", num_seqs=40, lengths=("lognormal", 600, 1.0, 1, 5000))
@@ -406,9 +441,10 @@ def test_balanced_is_deterministic_and_reuses_its_workspace():
     ws = abi.balanced_workspace(q, k, tables)
     outs = [abi.paged_decode_attention_balanced(q, k, v, tables, lens, w.scale, None, ws) for _ in range(10)]
     torch.cuda.synchronize()
+    want = oracle_out(w)
     for i, o in enumerate(outs):
-        assert torch.equal(o, outs[0]), f"run {i} differs"
-    assert max_err(outs[0], oracle_out(w)) <= TOL
+        assert float((o - outs[0]).abs().max()) <= 1e-5, f"run {i} differs"
+        assert max_err(o, want) <= TOL
     # a smaller batch on the same workspace
     small = abi.paged_decode_attention_balanced(q[:7].contiguous(), k, v, tables[:7].contiguous(),
                                                 lens[:7].contiguous(), w.scale, None, ws)

@@ -1,7 +1,8 @@
 """The entry point that allocates nothing: paged_decode_attention_balanced_static
 (the balanced schedule on the library's static device scratch) against
 paged_decode_attention_balanced with a caller workspace, through the C ABI,
-on two calls in a row, the second with a smaller input."""
+on two calls in a row, the second with a smaller input, and both against
+the oracle."""
 from __future__ import annotations
 
 import numpy as np
@@ -42,7 +43,9 @@ def test_static_scratch_matches_the_workspace_entry_on_two_calls():
     small = workloads.generate("qwen25_7b_prefix", num_seqs=5, lengths=("uniform", 1, 300))
     for w in (big, small):
         want, got = _both(w)
-        assert torch.equal(got, want)   # same kernels, same split points: same bits
+        # same kernels and split points; the waves' tile claims (and so the
+        # summation order) are settled at run time
+        assert float((got - want).abs().max()) <= 1e-5
         g = got.cpu().numpy().astype(np.float64)
         assert np.all(np.isfinite(g))
         assert float(np.max(np.abs(g - _oracle(w)))) <= TOL
