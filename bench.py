@@ -92,17 +92,43 @@ class HipEvents:
         self.ev = []
 
 
+def code_only(text: str) -> str:
+    """C/C++ source with its comments removed and each line's trailing
+    whitespace dropped (string and character literals kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = [ln.rstrip() for ln in "".join(out).split("\n")]
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_digest() -> str:
-    """Digest of the kernel and launch sources: every file under csrc/ except
-    abi.hip, the host-side ABI layer (argument checks, descriptors), whose
-    changes do not change what the kernels execute."""
+    """Digest of the kernel and launch sources: the code (comments and blank
+    lines left out) of every file under csrc/ except abi.hip, the host-side
+    ABI layer (argument checks, descriptors), whose changes do not change what
+    the kernels execute."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_gqa_cache_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name == "abi.hip":
             continue
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -933,8 +933,14 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
                                             kDeviceScope);
     // Count this partition once all its waves' partial stores are complete
     // at device scope; the workgroup that takes the last ticket merges.
-    // No cache maintenance is needed: the partials are written and read
-    // with device-scope accesses, and the counter is a device atomic.
+    // The ordering rests on the ISA's scope bits, not on a language-level
+    // release: the partials are stored and loaded with device scope (written
+    // through to, and read from, the device coherence point, past the XCD
+    // L2's own copies), every wave waits for its stores to complete before
+    // the barrier, and only then is the ticket (a device atomic) taken.  An
+    // acquire-release ticket would add an L2 write-back and invalidate per
+    // partition; measured, the B = 32 step went 23 -> 28 us and the fused
+    // headline layer 66 -> 124 us.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     int* counter = p.counters + static_cast<size_t>(b) * p.num_kv_heads + h;
@@ -1703,7 +1709,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_cu_stream(const DecodePa
     sh.lock[threadIdx.x] = 0;
   }
   if (threadIdx.x == 0) {
-    sh.next_unit = NW;   // units 0 .. NW - 1 are the waves' first, taken without the counter
+    sh.next_unit = 2 * NW;   // units w and NW + w are wave w's first two, taken without the counter
     sh.alloc_lock = 0;
   }
   // Exclusive prefix sum over sequences of Hkv * (tiles from the window's
@@ -1809,8 +1815,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_cu_stream(const DecodePa
     first.pk = 0;
     first.phase = 0;
   }
-  Cursor cur = first;
-  __syncthreads();   // slot tags, locks and the unit counter are set
+  Cursor cur = first;   // (the slot tags, locks and counter set above are visible: the prefix loop synchronised)
 
   const char* kcache = static_cast<const char*>(p.k_cache);
   const char* vcache = static_cast<const char*>(p.v_cache);
@@ -2052,7 +2057,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_cu_stream(const DecodePa
   claim(P, wid);
   if (P.n == 0) return;
   load_q(qop, P);
-  claim(N);
+  claim(N, NW + wid);
 #pragma unroll
   for (int k = 0; k < RD; ++k) load_tile(k, P, kCached);   // (a second-part first unit is cached too)
   // First phase: N's tiles cached.

@@ -45,3 +45,13 @@ def test_every_committed_kernel_profile_names_the_current_sources():
         text = open(path).read()
         found = re.findall(r"\b[0-9a-f]{16}\b", text)
         assert digest in found, f"{os.path.basename(path)} was taken from other kernel sources"
+
+
+def test_kernel_digest_reads_code_not_comments():
+    """A comment-only edit leaves the kernel-source digest unchanged (the
+    profiles stay valid); a code edit changes it."""
+    src = 'int a = 1; // x\n/* y */ const char* s = "p//q /* r */";\n\n  float f; /* z\n w */ int b;\n'
+    assert bench.code_only(src) == 'int a = 1;\n const char* s = "p//q /* r */";\n  float f;  int b;'
+    assert bench.code_only(src.replace("// x", "// another note")) == bench.code_only(src)
+    assert bench.code_only(src.replace("a = 1", "a = 2")) != bench.code_only(src)
+
