@@ -1,8 +1,10 @@
 """Build libpagedkv.so in-tree with hipcc for gfx950.
 
-    python -m paged_kv_gqa_cache_amd.build
+    python -m paged_kv_gqa_cache_amd.build [--host-sanitizers]
 
-Compiles every ``csrc/*.hip`` into ``paged_kv_gqa_cache_amd/libpagedkv.so``.
+Compiles every ``csrc/*.hip`` into ``paged_kv_gqa_cache_amd/libpagedkv.so``
+(with --host-sanitizers: ``libpagedkv_hostsan.so``, the host code built with
+AddressSanitizer and UndefinedBehaviorSanitizer, for the CPU tests).
 """
 from __future__ import annotations
 
@@ -30,14 +32,28 @@ HIPCC_FLAGS = [
 ]
 
 
+# Host-side sanitizer build (a CPU test target): AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host code only (argument validation,
+# descriptors, launch set-up); the device code is compiled as usual.
+HOSTSAN_LIB = os.path.join(HERE, "libpagedkv_hostsan.so")
+HOSTSAN_FLAGS = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
 def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, host_sanitizers: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *sources(), "-o", tmp]
+    out = HOSTSAN_LIB if host_sanitizers else LIB
+    tmp = out + ".tmp"
+    extra = HOSTSAN_FLAGS if host_sanitizers else []
+    cmd = [hipcc, *HIPCC_FLAGS, *extra, *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,10 +63,10 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    build()
+    build(host_sanitizers="--host-sanitizers" in sys.argv[1:])
     sys.exit(0)
