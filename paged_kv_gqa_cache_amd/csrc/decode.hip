@@ -42,6 +42,7 @@
 //  * Softmax runs in base 2 (log2 e folded into the scale).
 #include "pkv_common.h"
 #include "pkv_launch.h"
+#include "pkv_sched.h"
 
 #include <algorithm>
 #include <atomic>
@@ -1235,7 +1236,9 @@ __global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const Decode
   __shared__ int s_len[kMaxSeqsPersistent];       // context length
   __shared__ int s_q0[kMaxSeqsPersistent];        // first query row
   __shared__ int s_nq[kMaxSeqsPersistent];        // query rows
-  __shared__ int s_wsum[NW];
+  __shared__ int s_ccum[kMaxSeqsPersistent + 1];  // tiles of the items before sequence b
+  __shared__ int s_span[kMaxSeqsPersistent];      // tiles of one kv head's groups
+  __shared__ int s_wsum[2][NW];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int B = p.num_seqs;
@@ -1245,42 +1248,101 @@ __global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const Decode
     return n > 0 ? ((L + kBlockSize - 1) / kBlockSize + p.partition_blocks - 1) / p.partition_blocks : 0;
   };
 
-  int carry = 0;
+  // Exclusive prefix sums over sequences of the items and of their tiles
+  // (Hkv x the blocks every group reads: group_prefix).
+  int carry = 0, ccarry = 0;
   for (int c0 = 0; c0 < B; c0 += NW * 64) {
     const int i = c0 + static_cast<int>(threadIdx.x);
-    int items = 0;
+    int items = 0, cost = 0;
     if (i < B) {
       const int L = max(0, min(p.context_lens[i], p.mbps * kBlockSize));
       const int q0 = max(0, min(p.query_start[i], p.num_query_tokens));
       const int q1 = max(q0, min(p.query_start[i + 1], p.num_query_tokens));
       const int n = min(q1 - q0, L);
+      const int span = static_cast<int>(group_prefix(L, n, TPG, num_groups(n, TPG)));
       s_len[i] = L;
       s_q0[i] = q0;
       s_nq[i] = n;
-      items = Hkv * ((n + TPG - 1) / TPG) * parts_of(L, n);
+      s_span[i] = span;
+      items = Hkv * num_groups(n, TPG) * parts_of(L, n);
+      cost = Hkv * span;
     }
-    int x = items;
+    int x = items, y = cost;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off);
-      if (lane >= off) x += y;
+      const int xs = __shfl_up(x, off);
+      const int ys = __shfl_up(y, off);
+      if (lane >= off) {
+        x += xs;
+        y += ys;
+      }
     }
-    if (lane == 63) s_wsum[wid] = x;
+    if (lane == 63) {
+      s_wsum[0][wid] = x;
+      s_wsum[1][wid] = y;
+    }
     __syncthreads();
-    int before = carry;
-    for (int w = 0; w < wid; ++w) before += s_wsum[w];
-    int total = 0;
-    for (int w = 0; w < NW; ++w) total += s_wsum[w];
-    if (i < B) s_cum[i + 1] = before + x;
-    if (i == 0) s_cum[0] = 0;
+    int before = carry, cbefore = ccarry;
+    for (int w = 0; w < wid; ++w) {
+      before += s_wsum[0][w];
+      cbefore += s_wsum[1][w];
+    }
+    int total = 0, ctotal = 0;
+    for (int w = 0; w < NW; ++w) {
+      total += s_wsum[0][w];
+      ctotal += s_wsum[1][w];
+    }
+    if (i < B) {
+      s_cum[i + 1] = before + x;
+      s_ccum[i + 1] = cbefore + y;
+    }
+    if (i == 0) s_cum[0] = s_ccum[0] = 0;
     carry += total;
+    ccarry += ctotal;
     __syncthreads();
   }
   const int N = carry;
+  const int C = ccarry;
+  // With more items than workgroups, XCD ranges are cut by tiles, not by
+  // items: items (sequence, kv head, group, partition) differ in length
+  // with their sequence's context, and ranges of equal item counts left
+  // the most loaded wave 1.92x the mean (chunked prefill; 1.33x by tiles,
+  // host count; measured 214 -> 182 us).  With at most one item per
+  // workgroup the step is bound by its longest item whatever the ranges,
+  // and equal counts keep every workgroup at one item (speculative
+  // verification: 71 us, 76 by tiles).  First item at or after tile c of
+  // the item order.
+  auto item_at = [&](int64_t c) {
+    if (c >= C) return N;
+    int lo_b = 0, hi_b = B;
+    while (hi_b - lo_b > 1) {
+      const int mid = (lo_b + hi_b) >> 1;
+      if (s_ccum[mid] <= c) lo_b = mid;
+      else hi_b = mid;
+    }
+    const int b = lo_b;
+    const int L = s_len[b], n = s_nq[b];
+    const int ng = num_groups(n, TPG);
+    const int parts = parts_of(L, n);
+    const int rem = static_cast<int>(c - s_ccum[b]);
+    const int h = rem / s_span[b];
+    const int rem2 = rem - h * s_span[b];
+    int lo_g = 0, hi_g = ng;
+    while (hi_g - lo_g > 1) {
+      const int mid = (lo_g + hi_g) >> 1;
+      if (group_prefix(L, n, TPG, mid) <= rem2) lo_g = mid;
+      else hi_g = mid;
+    }
+    const int part = (rem2 - static_cast<int>(group_prefix(L, n, TPG, lo_g))) / p.partition_blocks;
+    return s_cum[b] + (h * ng + lo_g) * parts + min(part, parts - 1);
+  };
   const int xcd = blockIdx.x % kXcds;
   const int per_xcd = gridDim.x / kXcds;
-  const int lo = static_cast<int>(static_cast<int64_t>(N) * xcd / kXcds);
-  const int hi = static_cast<int>(static_cast<int64_t>(N) * (xcd + 1) / kXcds);
+  const bool by_tiles = N > static_cast<int>(gridDim.x);
+  const int lo = by_tiles ? item_at(static_cast<int64_t>(C) * xcd / kXcds)
+                          : static_cast<int>(static_cast<int64_t>(N) * xcd / kXcds);
+  const int hi = by_tiles ? item_at(static_cast<int64_t>(C) * (xcd + 1) / kXcds)
+                          : static_cast<int>(static_cast<int64_t>(N) * (xcd + 1) / kXcds);
   // Item n -> (sequence, kv head, group of packs, partition), partition fastest.
   auto locate = [&](int n, int& b, int& h, int& pack, int& part) {
     int lo_b = 0, hi_b = B;
