@@ -1303,15 +1303,17 @@ __global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const Decode
   }
   const int N = carry;
   const int C = ccarry;
-  // With more items than workgroups, XCD ranges are cut by tiles, not by
-  // items: items (sequence, kv head, group, partition) differ in length
+  // In one pass with more items than workgroups, XCD ranges are cut by
+  // tiles, not by items: items (sequence, kv head, group) differ in length
   // with their sequence's context, and ranges of equal item counts left
   // the most loaded wave 1.92x the mean (chunked prefill; 1.33x by tiles,
-  // host count; measured 214 -> 182 us).  With at most one item per
+  // host count; measured 214 -> 184 us).  With at most one item per
   // workgroup the step is bound by its longest item whatever the ranges,
   // and equal counts keep every workgroup at one item (speculative
-  // verification: 71 us, 76 by tiles).  First item at or after tile c of
-  // the item order.
+  // verification: 71 us, 76 by tiles).  Partitioned items are capped at a
+  // partition's blocks, so counts already track tiles (by tiles: 1.42x ->
+  // 1.55x on the host count, P = 1024 242 -> 285 us).  First item at or
+  // after tile c of the item order.
   auto item_at = [&](int64_t c) {
     if (c >= C) return N;
     int lo_b = 0, hi_b = B;
@@ -1338,7 +1340,7 @@ __global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const Decode
   };
   const int xcd = blockIdx.x % kXcds;
   const int per_xcd = gridDim.x / kXcds;
-  const bool by_tiles = N > static_cast<int>(gridDim.x);
+  const bool by_tiles = MODE == MODE_FINAL && N > static_cast<int>(gridDim.x);
   const int lo = by_tiles ? item_at(static_cast<int64_t>(C) * xcd / kXcds)
                           : static_cast<int>(static_cast<int64_t>(N) * xcd / kXcds);
   const int hi = by_tiles ? item_at(static_cast<int64_t>(C) * (xcd + 1) / kXcds)
