@@ -820,11 +820,12 @@ __device__ __forceinline__ void merge_waves(float m_run, float l_run, const f32x
   }
 }
 
-// The fused step's new token of sequence b into slot `off` of physical
-// block `blk`: kv head h's K and V rows of k_new / v_new, laid out as the
-// tiles are (one wave; lane c moves 16-byte chunk c of the rows).
+// The fused step's new token of sequence b into slot `off` of its block
+// `last` (the physical block its table names, skipped when out of range):
+// kv head h's K and V rows of k_new / v_new, laid out as the tiles are (one
+// wave; lane c moves 16-byte chunk c of the rows).
 template <int KVT, int D>
-__device__ __forceinline__ void write_new_token(const DecodeParams& p, int b, int h, int blk, int off) {
+__device__ __forceinline__ void write_new_token(const DecodeParams& p, int b, int h, int last, int off) {
   if constexpr (KVT != KV_E4M3) {   // E4M3 pools take their tokens through kv_cache_append_e4m3
     constexpr int E = ElemBytes<KVT>::value;
     typedef typename std::conditional<E == 4, uint32_t, uint16_t>::type Elem;
@@ -832,13 +833,17 @@ __device__ __forceinline__ void write_new_token(const DecodeParams& p, int b, in
     constexpr int CH = D / X;   // chunks per row
     const int lane = threadIdx.x & 63;
     if (lane < CH) {
+      // The block id and the new K and V rows load together (none depends
+      // on another): one round trip before the stores, not two.
+      const int blk = p.block_tables[static_cast<size_t>(b) * p.mbps + last];
       const size_t row = (static_cast<size_t>(b) * p.num_kv_heads + h) * D * E + lane * 16;
+      const u32x4 kv = ld16(static_cast<const char*>(p.k_new) + row);
+      const u32x4 vv = ld16(static_cast<const char*>(p.v_new) + row);
+      if (blk < 0 || blk >= p.num_blocks) return;
       const size_t tile = (static_cast<size_t>(blk) * p.num_kv_heads + h) * kBlockSize * D * E;
       char* kc = static_cast<char*>(const_cast<void*>(p.k_cache));
       char* vc = static_cast<char*>(const_cast<void*>(p.v_cache));
-      st16(kc + tile + (static_cast<size_t>(lane) * kBlockSize + off) * 16,
-           ld16(static_cast<const char*>(p.k_new) + row));
-      const u32x4 vv = ld16(static_cast<const char*>(p.v_new) + row);
+      st16(kc + tile + (static_cast<size_t>(lane) * kBlockSize + off) * 16, kv);
       Elem vals[X];
       __builtin_memcpy(vals, &vv, 16);
       Elem* vt = reinterpret_cast<Elem*>(vc + tile);
@@ -887,8 +892,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int b, int h,
   if (MODE == MODE_SPLIT && p.k_new != nullptr) {
     const int last = (L - 1) / kBlockSize;
     if (last >= blk0 && last < blk1) {   // workgroup-uniform
-      const int id = p.block_tables[static_cast<size_t>(b) * p.mbps + last];
-      if (wid == 0 && id >= 0 && id < p.num_blocks) write_new_token<KVT, D>(p, b, h, id, (L - 1) % kBlockSize);
+      if (wid == 0) write_new_token<KVT, D>(p, b, h, last, (L - 1) % kBlockSize);
       __syncthreads();
     }
   }
