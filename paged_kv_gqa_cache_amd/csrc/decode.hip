@@ -88,14 +88,37 @@ template <int KVT, int D> struct Tile16 {
       vt[m].x &= m01; vt[m].y &= m23; vt[m].z &= m01; vt[m].w &= m23;
     }
   }
+  // P as hi + lo 16-bit parts: hi = p rounded to the 16-bit type, lo =
+  // (p - hi) rounded.  For bf16 the float value of hi is its bits moved to
+  // the top half, read off the packed pair, not a second conversion.
+  template <typename VN, int N>
+  __device__ static void split_p(const float (&p)[N], VN& hi, VN& lo) {
+    if constexpr (kBf16) {
+      typedef float F2 __attribute__((ext_vector_type(2)));
+      typedef __bf16 B2 __attribute__((ext_vector_type(2)));
+      typedef uint32_t UW __attribute__((ext_vector_type(N / 2)));
+      UW hw, lw;
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        const uint32_t w = bitcast<uint32_t>(__builtin_convertvector(F2{p[2 * i], p[2 * i + 1]}, B2));
+        hw[i] = w;
+        const F2 r = {p[2 * i] - __uint_as_float(w << 16), p[2 * i + 1] - __uint_as_float(w & 0xFFFF0000u)};
+        lw[i] = bitcast<uint32_t>(__builtin_convertvector(r, B2));
+      }
+      hi = bitcast<VN>(hw);
+      lo = bitcast<VN>(lw);
+    } else {
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const S h = static_cast<S>(p[j]);
+        hi[j] = h;
+        lo[j] = static_cast<S>(p[j] - static_cast<float>(h));
+      }
+    }
+  }
   __device__ static void pv(f32x4 (&o)[NT], const u32x4 (&vt)[NLOAD], const float (&p)[4], float) {
     V4 hi, lo;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const S h = static_cast<S>(p[j]);
-      hi[j] = h;
-      lo[j] = static_cast<S>(p[j] - static_cast<float>(h));
-    }
+    split_p(p, hi, lo);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const u32x2 a = (n & 1) ? u32x2{vt[n >> 1].z, vt[n >> 1].w} : u32x2{vt[n >> 1].x, vt[n >> 1].y};
@@ -116,12 +139,7 @@ template <int KVT, int D> struct Tile16 {
   __device__ static void pv2(f32x4 (&o)[NT], const u32x4 (&va)[NLOAD], const u32x4 (&vb)[NLOAD],
                              const float (&p)[8]) {
     V8 hi, lo;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const S h = static_cast<S>(p[j]);
-      hi[j] = h;
-      lo[j] = static_cast<S>(p[j] - static_cast<float>(h));
-    }
+    split_p(p, hi, lo);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const u32x4 a = (n & 1) ? u32x4{va[n >> 1].z, va[n >> 1].w, vb[n >> 1].z, vb[n >> 1].w}
@@ -562,6 +580,9 @@ __device__ __forceinline__ void attend_packs(const DecodeParams& p, int b, int h
   int lim_lo[NPK];
 #pragma unroll
   for (int k = 0; k < NPK; ++k) lim_lo[k] = CAUSAL ? __builtin_amdgcn_readfirstlane(lim[k]) : 0;
+  int lim_min = lim_lo[0];
+#pragma unroll
+  for (int k = 1; k < NPK; ++k) lim_min = min(lim_min, lim_lo[k]);
 
   auto process = [&](const u32x4 (&kt)[NL], u32x4 (&vt)[NL], float ksc, float vsc, int i) {
     const int tok0 = (first + stride * i) * kBlockSize;
@@ -673,12 +694,25 @@ __device__ __forceinline__ void attend_packs(const DecodeParams& p, int b, int h
       {
         const int i0 = __builtin_amdgcn_readlane(ids, 0);
         const int i1 = __builtin_amdgcn_readlane(ids, min(1, cnt - 1));
+        // K before V, as the loop issues them (the next pair's K after
+        // the scores, its V after PV): the memory counter drains in
+        // issue order, so with the same order on entry the wait before
+        // the scores covers only the K loads.  Left to the scheduler, the
+        // first pair's V went first, and the wait merged at the loop head
+        // drained everything, the V just issued included, every pair.
         load_half(kb[0], kcache, i0, true);
-        load_half(vb[0], vcache, i0, true);
         load_half(kb[1], kcache, i1, 1 < cnt);
+        __builtin_amdgcn_sched_barrier(0);
+        load_half(vb[0], vcache, i0, true);
         load_half(vb[1], vcache, i1, 1 < cnt);
       }
-      for (int i = 0; i < cnt; i += 2) {
+      // One pair.  MASKED: the general form; otherwise the pair is known
+      // to need no mask (both tiles whole, inside the window and at or
+      // below every column's causal limit), and the body carries none of
+      // the per-lane compares, which the compiler would issue ahead of the
+      // (rarely taken) masking branches.
+      auto pair = [&](int i, auto masked) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked)::value;
         const bool two = i + 1 < cnt;   // else tile b is a zero-size load: V = 0, its logits masked
         const int tok0 = (first + stride * (base + i)) * kBlockSize;
         const int tok1 = tok0 + stride * kBlockSize;
@@ -692,16 +726,26 @@ __device__ __forceinline__ void attend_packs(const DecodeParams& p, int b, int h
         const int n3 = __builtin_amdgcn_readlane(ids, min(i + 3, cnt - 1));
         load_half(kb[0], kcache, n2, i + 2 < cnt);
         load_half(kb[1], kcache, n3, i + 3 < cnt);
-        if (tok0 + kBlockSize > L) T::mask_v(vb[0], L - tok0 - 4 * g);
-        if (two && tok1 + kBlockSize > L) T::mask_v(vb[1], L - tok1 - 4 * g);
+        if constexpr (MASKED) {
+          if (tok0 + kBlockSize > L) T::mask_v(vb[0], L - tok0 - 4 * g);
+          if (two && tok1 + kBlockSize > L) T::mask_v(vb[1], L - tok1 - 4 * g);
+        }
 #pragma unroll
         for (int k = 0; k < NPK; ++k) {
           float x[8];
-          logits(sa[k], x, tok0, k);
-          logits(sb[k], x + 4, tok1, k);
-          if (!two) {
+          if constexpr (MASKED) {
+            logits(sa[k], x, tok0, k);
+            logits(sb[k], x + 4, tok1, k);
+            if (!two) {
 #pragma unroll
-            for (int j = 4; j < 8; ++j) x[j] = -INFINITY;
+              for (int j = 4; j < 8; ++j) x[j] = -INFINITY;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              x[j] = sa[k][j] * p.qk_scale_log2;
+              x[4 + j] = sb[k][j] * p.qk_scale_log2;
+            }
           }
           WaveState<NT>& sk = st[k];
           const float bm = max_over_groups(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
@@ -722,7 +766,20 @@ __device__ __forceinline__ void attend_packs(const DecodeParams& p, int b, int h
         }
         load_half(vb[0], vcache, n2, i + 2 < cnt);
         load_half(vb[1], vcache, n3, i + 3 < cnt);
-      }
+      };
+      // The pairs that need no mask form one run (positions only grow with
+      // i): masked pairs before it (the window's first block), the run,
+      // masked pairs after it (the causal diagonal, the context's tail).
+      auto clean = [&](int i) __attribute__((always_inline)) {
+        const int tok0 = (first + stride * (base + i)) * kBlockSize;
+        const int tok1 = tok0 + stride * kBlockSize;
+        return i + 1 < cnt && tok1 + kBlockSize <= L && tok0 >= lo &&
+               (!CAUSAL || tok1 + kBlockSize - 1 <= lim_min);
+      };
+      int i = 0;
+      for (; i < cnt && !clean(i); i += 2) pair(i, std::true_type{});
+      for (; i < cnt && clean(i); i += 2) pair(i, std::false_type{});
+      for (; i < cnt; i += 2) pair(i, std::true_type{});
     }
     return;
   }
@@ -1234,7 +1291,8 @@ __device__ __forceinline__ void prefill_item(const DecodeParams& p, int b, int h
 // paged_decode_persistent: LDS prefix sums of each sequence's items, XCD
 // ranges.
 template <int KVT, int D, int NW, int MODE, int PF, int NPK, bool PAIRS>
-__global__ __launch_bounds__(NW * 64) void paged_prefill_persistent(const DecodeParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KVT == KV_F32 ? 1 : 2)))
+void paged_prefill_persistent(const DecodeParams p) {
   __shared__ ItemShared<NW, D / 16> sm;
   __shared__ int s_cum[kMaxSeqsPersistent + 1];   // items before sequence b
   __shared__ int s_len[kMaxSeqsPersistent];       // context length
