@@ -224,7 +224,11 @@ int kv_cache_copy_blocks(const int32_t* block_mapping, int32_t num_pairs, void* 
  *                 "Projects", row 05: page scales, fused dequantisation)
  *   out           [B][Hq][D] in out_dtype
  * One workgroup per (sequence, kv head): suited to short contexts or many
- * sequences; for long contexts use the partial/reduce pair.
+ * sequences of similar length.  The longest sequence's item bounds the
+ * step, so for a ragged batch (lengths spread over decades) or long
+ * contexts use paged_decode_attention_balanced (or its _static form, which
+ * needs no workspace argument): on a 128-sequence layer with lognormal
+ * lengths it runs twice as fast as this one pass.
  */
 int paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, const int32_t* context_lens,
