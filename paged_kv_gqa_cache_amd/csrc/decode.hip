@@ -1289,7 +1289,9 @@ __device__ __forceinline__ void prefill_item(const DecodeParams& p, int b, int h
 
 // Persistent form of the multi-token step, laid out like
 // paged_decode_persistent: LDS prefix sums of each sequence's items, XCD
-// ranges.
+// ranges.  16-bit caches are held to 256 registers, two waves per SIMD (the
+// pair loop's three runs of pairs otherwise drift a few registers past it
+// and halve the waves); f32 tiles need more than that.
 template <int KVT, int D, int NW, int MODE, int PF, int NPK, bool PAIRS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KVT == KV_F32 ? 1 : 2)))
 void paged_prefill_persistent(const DecodeParams p) {
