@@ -839,6 +839,23 @@ def test_prefill_whole_context_new_and_16bit_output():
     assert torch.all((o16.float() - r.float()).abs() <= ulp)
 
 
+@pytest.mark.parametrize("rows", [(24, 40), (2, 6)])
+def test_prefill_long_contexts_cross_block_id_chunks(rows):
+    """Contexts past 4096 tokens: each wave reads more than 64 blocks, so its
+    block ids arrive in several 64-entry chunks and the tile loop restarts
+    per chunk (with tile pairs, the runs of masked and unmasked pairs too).
+    Both tile paths (16+ rows per sequence: pairs), one pass and
+    partitioned."""
+    _announce("prefill long contexts", rows)
+    w = workloads.generate("qwen25_7b_chunk", num_seqs=3, lengths=("uniform", 5000, 9000),
+                           query_tokens=("uniform", *rows))
+    assert w.context_lens.max() > 4096
+    want = _prefill_oracle(w)
+    pool = gpu_pool(w)
+    for P in (0, 2048):
+        assert max_err(_prefill_gpu(w, pool, P), want) <= TOL, P
+
+
 def test_prefill_full_size_sampled():
     """The 16-sequence chunked-prefill workload at full size, in one pass (the
     benchmarked configuration) and partitioned, checked on three sequences'
