@@ -922,6 +922,51 @@ def test_decode_step_equals_write_then_split(name, P):
     assert max_err(ob, oracle_out(w)) <= TOL
 
 
+@pytest.mark.parametrize("name,mode", [("tiny", "step"), ("smollm2_360m", "fused"), ("qwen25_7b_prefix", "balanced")])
+def test_steps_replay_from_a_graph(name, mode):
+    """Steps captured in a HIP graph (as the bench's graph figures replay
+    them): every replay, with eager work and a synchronisation between
+    replays, equals the eager call, output and cache, bit for bit for the
+    one-launch paths (the step's new-token write lands on the same slot each
+    time; the split counters return to zero inside the kernel, so no memory
+    clear is recorded) and within 1e-5 for the balanced schedule."""
+    _announce("graph replay", name, mode)
+    from paged_kv_gqa_cache_amd import abi
+    w = workloads.generate(name, **REDUCED[name])
+    s = w.spec
+    P = s.partition_size
+    k, v, sc = gpu_pool(w, with_new_tokens=(mode != "step"))
+    q, tables, lens = inputs(w)
+    ws = abi.split_workspace(q, k, tables, P).zero_()
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    if mode == "step":
+        nk, nv = to_dev(w.new_k, s.kv_dtype), to_dev(w.new_v, s.kv_dtype)
+        call = lambda: abi.paged_decode_step(q, nk, nv, k, v, tables, lens, w.scale, P, ws, out=out)
+    elif mode == "fused":
+        call = lambda: abi.paged_decode_attention_split(q, k, v, tables, lens, w.scale, sc, P, ws, out=out)
+    else:   # the balanced schedule's two launches (its workspace needs no clearing)
+        bws = abi.balanced_workspace(q, k, tables)
+        call = lambda: abi.paged_decode_attention_balanced(q, k, v, tables, lens, w.scale, sc, bws, out=out)
+    call()
+    torch.cuda.synchronize()
+    want_out, want_k, want_v = out.clone(), k.clone(), v.clone()
+    assert max_err(want_out, oracle_out(w)) <= TOL
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        if mode == "balanced":   # its waves claim tiles at run time: fp32 sums in varying order
+            assert float((out - want_out).abs().max()) <= 1e-5, rep
+        else:
+            assert torch.equal(out, want_out), rep
+        assert _same_bits(k, want_k) and _same_bits(v, want_v), rep
+        decode(w, (k, v, sc), "single")   # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_decode_step_with_window_and_repeated_calls():
     """Sliding window, and the same workspace reused across calls (the split
     counters return to zero): every call equals the two-launch result."""
