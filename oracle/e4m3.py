@@ -16,7 +16,7 @@ follows the OCP 8-bit floating point specification (OFP8, v1.0) for E4M3:
   NaN; there are no infinities, so the largest finite magnitude is
   2^8 * 1.75 = 448.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * the format is OCP E4M3FN (max 448), not the FNUZ variant (max 240): the
   per-block scale amax/448 only makes sense for a maximum of 448;
@@ -124,7 +124,7 @@ def append_token(block_codes: np.ndarray, scale, offset: int, x: np.ndarray):
     ``offset``.  Returns ``(codes, scale)`` after the step.
 
     The pages fix a scale per page and head but no append policy.  Reading
-    taken (listed in the design doc): the block keeps the bulk quantiser's
+    taken: the block keeps the bulk quantiser's
     invariant scale = fp32(amax / 448) over its tokens so far, 1 while they
     are all zero.  The token's own s = fp32(amax(|x|) / 448).  When the token
     is the block's first, or every earlier code of the block is a zero
