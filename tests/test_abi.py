@@ -31,6 +31,19 @@ def test_every_declared_function_is_exported():
     assert set(abi.EXPORTED) == set(names)
 
 
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No CPU fallback: with the library absent, importing the binding
+    raises (a fresh interpreter, the library path pointed at nothing)."""
+    import subprocess
+    import sys
+    env = dict(os.environ, PAGEDKV_LIB=str(tmp_path / "libpagedkv.so"))
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, "-c", "import paged_kv_gqa_cache_amd.abi"], cwd=root, env=env,
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode != 0
+    assert "ImportError" in res.stderr and "is not built" in res.stderr
+
+
 def test_version():
     assert "gfx950" in abi.version()
 
