@@ -255,6 +255,15 @@ class Runner:
         ev.close()
         return wall / steps, kernel_ms
 
+    def run_graph_or_none(self, steps: int, warmup: int):
+        """``run_graph``, or (None, the error) if capture fails: the graph
+        figure is an extra, never a reason to lose the line."""
+        try:
+            return self.run_graph(steps, warmup), None
+        except Exception as e:   # noqa: BLE001 (reported in the line)
+            self.torch.cuda.synchronize()
+            return None, f"{type(e).__name__}: {e}"[:200]
+
     def run_graph(self, steps: int, warmup: int) -> float:
         """Seconds per step with the steps replayed from a HIP graph: one
         captured step per layer pool (same arguments as ``step``), the graph
@@ -524,8 +533,11 @@ def measure_rows(args, only=None) -> dict:
         # The same steps replayed from a captured graph: launch-bound layers
         # are paced by the host's per-call work, which a serving loop that
         # captures its decode step does not pay.
-        tg = r.run_graph(steps, warm)
-        row.update({"graph_us_per_step": round(tg * 1e6, 2), "graph_seqs_layers_per_s": round(r.spec.num_seqs / tg, 1)})
+        tg, gerr = r.run_graph_or_none(steps, warm)
+        row.update({"graph_us_per_step": None if tg is None else round(tg * 1e6, 2),
+                    "graph_seqs_layers_per_s": None if tg is None else round(r.spec.num_seqs / tg, 1)})
+        if gerr:
+            row["graph_error"] = gerr
         rows[key] = row
         del r
         torch.cuda.empty_cache()
@@ -810,7 +822,7 @@ def main():
     r = Runner(args.workload, args.layers, args.partition_size, args.path)
     t_step, part_ms = r.run(args.steps, args.warmup)
     part_avg = sum(part_ms) / len(part_ms)
-    t_graph = r.run_graph(args.steps, args.warmup)   # the same steps replayed from a captured graph
+    t_graph, graph_err = r.run_graph_or_none(args.steps, args.warmup)   # the same steps replayed from a captured graph
     value = r.unique_bytes / t_step / 1e9
     achieved = r.unique_bytes / (part_avg * 1e-3) / 1e9
     s = r.spec
@@ -820,11 +832,11 @@ def main():
         r2 = Runner(SECONDARY, args.layers, None, args.secondary_path)
         t2, p2 = r2.run(args.steps, args.warmup)
         k2 = sum(p2) / len(p2)
-        t2g = r2.run_graph(args.steps, args.warmup)
+        t2g, _ = r2.run_graph_or_none(args.steps, args.warmup)
         b32 = {"workload": f"{SECONDARY}: {DESCRIPTIONS[SECONDARY]}", "path": args.secondary_path,
                "partition_size": None if args.secondary_path == "balanced" else r2.P,
                "us_per_step": round(t2 * 1e6, 2),
-               "graph_us_per_step": round(t2g * 1e6, 2),
+               "graph_us_per_step": None if t2g is None else round(t2g * 1e6, 2),
                "dominant_kernel_us": round(k2 * 1e3, 2),
                "kv_GBps": round(r2.unique_bytes / t2 / 1e9, 1),
                "seqs_layers_per_s": round(r2.spec.num_seqs / t2, 1),
@@ -872,7 +884,7 @@ def main():
             "kv_bytes_unique": r.unique_bytes, "kv_bytes_logical": r.logical_bytes,
         },
         "us_per_step": round(t_step * 1e6, 2),
-        "graph_us_per_step": round(t_graph * 1e6, 2),
+        "graph_us_per_step": None if t_graph is None else round(t_graph * 1e6, 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 1),
         "seqs_layers_per_s": round(s.num_seqs / t_step, 1),
         "logical_GBps": round(r.logical_bytes / t_step / 1e9, 1),
@@ -900,6 +912,8 @@ def main():
         ceiling = read_ceiling()
         ceiling["kernel_frac_of_it"] = round(achieved / ceiling["GBps"], 4)
         line["read_ceiling"] = ceiling
+    if graph_err:
+        line["graph_error"] = graph_err
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(line), flush=True)
